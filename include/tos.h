@@ -1,0 +1,136 @@
+/*
+ * tos.h -- C ABI of libtos.so: fused attention forward pass with the tensorized
+ * online softmax, for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (FlashAttention-T page, section A3 "fused attention algorithm
+ * flow" and Fig 2(a); section A2 "tensorized online softmax", Algorithm 1):
+ *
+ *   O[b,h,i,:] = sum_j softmax_j(scale * <q_i, k_j>) v_j
+ *   lse[b,h,i] = ln sum_j exp(scale * <q_i, k_j>)
+ *
+ * over the valid keys j (all j < N, or j <= i when causal).  The softmax runs
+ * online over blocks of keys with the surrogate maximum of section A2: the
+ * subtracted maximum is the largest running row maximum over an X-row tile, so
+ * the rescale of O is one uniform factor exp2(c*(m^_old - m^)) per tile and
+ * Z = c*S - c*m^ feeds exp2 (c = scale*log2(e)).  An optional per-row fallback
+ * guards against the all-underflow case of section A2 ("numerical stability
+ * guarantees").
+ *
+ * Conventions for every entry point:
+ *   - Tensors are contiguous row-major [B][H][N][d] (q, k, v, o) and [B][H][N]
+ *     (lse), in device memory (hipMalloc / torch CUDA tensors).  Base pointers
+ *     are 16-byte aligned.  Self-attention only: queries and keys share N.
+ *   - The caller owns every buffer.  The library allocates no device memory,
+ *     keeps no pointer after returning, and holds no mutable global state.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *     the call returns without synchronising.  A device fault surfaces at the
+ *     caller's next synchronisation.
+ *   - Arguments are validated before anything is launched: on any error status
+ *     nothing has been written.
+ *   - Thread safety: calls may be made concurrently from several host threads.
+ */
+#ifndef TOS_H
+#define TOS_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TOS_VERSION 1
+
+typedef enum {
+    TOS_OK = 0,
+    TOS_ERR_INVALID_ARG = 1,   /* null required pointer, negative size, bad scale,
+                                  aliasing output, misaligned pointer, bad option  */
+    TOS_ERR_UNSUPPORTED = 2,   /* valid request outside what the kernels cover
+                                  (head dim not 64/128, size limits, option not
+                                  available for the dtype)                        */
+    TOS_ERR_HIP = 3            /* the HIP runtime rejected the launch             */
+} tos_status;
+
+typedef enum {
+    TOS_F32 = 0,       /* q, k, v, o: float32                                       */
+    TOS_BF16 = 1,      /* q, k, v, o: bfloat16                                      */
+    TOS_FP8_E4M3 = 2   /* q, k, v: OCP float8 e4m3fn codes (x = descale * code);
+                          o: bfloat16; descales are required in the options       */
+} tos_dtype;
+
+/* How the softmax row sum l is computed (FlashAttention-T section A2,
+ * "row-sum reduction", Fig 5(b)). */
+typedef enum {
+    TOS_SPLIT_VALU = 0,         /* vector-unit adds of P~ in fp32                   */
+    TOS_SPLIT_ROWSUM_MFMA = 1   /* matrix-unit contraction of the packed P~ against a
+                                   constant all-ones operand (bf16 only)            */
+} tos_softmax_split;
+
+/* All-underflow handling (FlashAttention-T section A2, "numerical stability
+ * guarantees": an implementation may fall back to per-row computation). */
+typedef enum {
+    TOS_FALLBACK_OFF = 0,    /* surrogate maximum throughout; a row whose
+                                exponentials all underflow gets O = 0, lse = -inf  */
+    TOS_FALLBACK_AUTO = 1,   /* per tile and key block, before exponentiating: if
+                                c*(m^_new - min_i m_i) > tau the tile switches, for
+                                the rest of the pass, to per-row maxima            */
+    TOS_FALLBACK_FORCE = 2   /* per-row maxima from the first block                 */
+} tos_fallback;
+
+typedef struct {
+    int size;              /* sizeof(tos_fwd_opts): the struct version             */
+    int x_tile;            /* surrogate tile rows X: 0 = default (32), 1, 16 or 32;
+                              X = 1 is the per-row online softmax                  */
+    int softmax_split;     /* a tos_softmax_split value                             */
+    int fallback;          /* a tos_fallback value                                  */
+    float fallback_tau;    /* AUTO threshold in log2 units; 0 = default (100 for
+                              f32/bf16 P~, 12 for e4m3 P~)                          */
+    float q_descale;       /* fp8 only: real value = descale * stored code; > 0    */
+    float k_descale;
+    float v_descale;
+    int* fallback_tiles;   /* NULL, or a device int the kernels add to, once per
+                              X-row tile that ran with per-row maxima (AUTO switch
+                              or FORCE).  The caller zeroes it.                    */
+} tos_fwd_opts;
+
+/*
+ * tos_attn_fwd -- O = softmax(scale * Q K^T) V and lse, as described above.
+ *
+ *   q, k, v   device pointers, [B][H][N][d] of `dtype` (see tos_dtype)
+ *   o         device pointer, [B][H][N][d]: float32 for TOS_F32, bfloat16
+ *             otherwise; must not overlap q, k, v or lse
+ *   lse       device pointer to [B][H][N] float32 natural-log log-sum-exp of the
+ *             scaled logits, or NULL to skip it
+ *   B, H, N   batch, heads, sequence length; >= 0 (any zero: nothing to do,
+ *             TOS_OK); B*H*ceil(N/128) must stay below 2^31
+ *   d         head dimension: 64 or 128
+ *   causal    0: every key; 1: key j <= query i (top-left aligned)
+ *   scale     softmax scale applied to <q, k>; finite and > 0
+ *   dtype     a tos_dtype value
+ *   opts      NULL for defaults (X = 32, VALU row sum, no fallback), or options
+ *   stream    hipStream_t to enqueue on
+ *
+ * Returns TOS_OK or an error status; see tos_status.
+ */
+tos_status tos_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
+                        tos_dtype dtype, const tos_fwd_opts* opts, void* stream);
+
+/* Fills *opts with the defaults (size set, X = 32, VALU, fallback off,
+ * descales 1).  Returns TOS_ERR_INVALID_ARG for NULL. */
+tos_status tos_fwd_opts_default(tos_fwd_opts* opts);
+
+/* Algorithmic matrix-unit work of one call: 4*B*H*N^2*d flops, halved when
+ * causal (the throughput metric's convention). */
+double tos_attn_fwd_flops(int64_t B, int64_t H, int64_t N, int64_t d, int causal);
+
+/* A static, human-readable name for a status code. */
+const char* tos_status_string(tos_status status);
+
+/* TOS_VERSION of the built library. */
+int tos_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TOS_H */

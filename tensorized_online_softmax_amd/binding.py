@@ -1,0 +1,159 @@
+"""ctypes binding of libtos.so (include/tos.h): argument marshalling only.
+
+Every step of the attention pass runs in the library's HIP kernels.  torch is
+used only to hand over device memory and the current HIP stream.  The binding
+raises if the built library is missing; there is no other code path.
+"""
+import ctypes
+import math
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libtos.so")
+
+TOS_OK, TOS_ERR_INVALID_ARG, TOS_ERR_UNSUPPORTED, TOS_ERR_HIP = 0, 1, 2, 3
+TOS_F32, TOS_BF16, TOS_FP8_E4M3 = 0, 1, 2
+TOS_SPLIT_VALU, TOS_SPLIT_ROWSUM_MFMA = 0, 1
+TOS_FALLBACK_OFF, TOS_FALLBACK_AUTO, TOS_FALLBACK_FORCE = 0, 1, 2
+
+EXPORTED = ("tos_attn_fwd", "tos_fwd_opts_default", "tos_attn_fwd_flops",
+            "tos_status_string", "tos_version")
+
+
+class tos_fwd_opts(ctypes.Structure):
+    _fields_ = [("size", ctypes.c_int), ("x_tile", ctypes.c_int),
+                ("softmax_split", ctypes.c_int), ("fallback", ctypes.c_int),
+                ("fallback_tau", ctypes.c_float), ("q_descale", ctypes.c_float),
+                ("k_descale", ctypes.c_float), ("v_descale", ctypes.c_float),
+                ("fallback_tiles", ctypes.c_void_p)]
+
+
+class TosError(RuntimeError):
+    def __init__(self, status):
+        self.status = status
+        super().__init__(tos_status_string(status))
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        # torch first: libtos.so must bind to the HIP runtime torch already
+        # loaded (same soname), so that torch's streams and allocations are
+        # valid handles for the library's launches
+        import torch  # noqa: F401
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it first "
+                               "(python -c 'import __graft_entry__ as g; g.build()')")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64 = ctypes.c_void_p, ctypes.c_int64
+        L.tos_attn_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int,
+                                   ctypes.c_float, ctypes.c_int, ctypes.POINTER(tos_fwd_opts), vp]
+        L.tos_attn_fwd.restype = ctypes.c_int
+        L.tos_fwd_opts_default.argtypes = [ctypes.POINTER(tos_fwd_opts)]
+        L.tos_fwd_opts_default.restype = ctypes.c_int
+        L.tos_attn_fwd_flops.argtypes = [i64, i64, i64, i64, ctypes.c_int]
+        L.tos_attn_fwd_flops.restype = ctypes.c_double
+        L.tos_status_string.argtypes = [ctypes.c_int]
+        L.tos_status_string.restype = ctypes.c_char_p
+        L.tos_version.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _ptr(x):
+    """A device pointer from a torch tensor, an int address, or None."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def tos_fwd_opts_default():
+    o = tos_fwd_opts()
+    rc = lib().tos_fwd_opts_default(ctypes.byref(o))
+    if rc != TOS_OK:
+        raise TosError(rc)
+    return o
+
+
+def tos_attn_fwd(q, k, v, o, lse, B, H, N, d, causal, scale, dtype, opts=None, stream=None):
+    """Direct call of the C entry point; returns the tos_status code."""
+    return lib().tos_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H),
+                              int(N), int(d), int(causal), float(scale), int(dtype),
+                              ctypes.byref(opts) if opts is not None else None, _stream(stream))
+
+
+def tos_attn_fwd_flops(B, H, N, d, causal):
+    return float(lib().tos_attn_fwd_flops(int(B), int(H), int(N), int(d), int(causal)))
+
+
+def tos_status_string(status):
+    return lib().tos_status_string(int(status)).decode()
+
+
+def tos_version():
+    return int(lib().tos_version())
+
+
+_DTYPE_CODES = {"f32": TOS_F32, "bf16": TOS_BF16, "fp8": TOS_FP8_E4M3}
+_SPLITS = {"valu": TOS_SPLIT_VALU, "rowsum_mfma": TOS_SPLIT_ROWSUM_MFMA}
+_FALLBACKS = {"off": TOS_FALLBACK_OFF, "auto": TOS_FALLBACK_AUTO, "force": TOS_FALLBACK_FORCE}
+
+
+def make_opts(x_tile=32, split="valu", fallback="off", tau=0.0, descale=None,
+              fallback_tiles=None):
+    op = tos_fwd_opts_default()
+    op.x_tile = int(x_tile)
+    op.softmax_split = _SPLITS[split]
+    op.fallback = _FALLBACKS[fallback]
+    op.fallback_tau = float(tau)
+    if descale is not None:
+        op.q_descale, op.k_descale, op.v_descale = (float(descale[n]) for n in ("q", "k", "v"))
+    op.fallback_tiles = _ptr(fallback_tiles)
+    return op
+
+
+def attn_fwd(q, k, v, causal=False, scale=None, dtype=None, x_tile=32, split="valu",
+             fallback="off", tau=0.0, descale=None, with_lse=True, fallback_tiles=None,
+             out=None, lse=None, stream=None):
+    """Allocate O (and lse) with torch and run tos_attn_fwd on the current stream.
+
+    q, k, v: contiguous CUDA tensors [B, H, N, d] of float32, bfloat16 or
+    float8_e4m3fn (then `descale` = {"q":..., "k":..., "v":...} is required).
+    Returns (o, lse); lse is None when with_lse is False.
+    """
+    import torch
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must all be [B, H, N, d]")
+    B, H, N, d = q.shape
+    if dtype is None:
+        dtype = {torch.float32: "f32", torch.bfloat16: "bf16",
+                 torch.float8_e4m3fn: "fp8"}[q.dtype]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    odt = torch.float32 if dtype == "f32" else torch.bfloat16
+    o = out if out is not None else torch.empty((B, H, N, d), dtype=odt, device=q.device)
+    if with_lse and lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if not with_lse:
+        lse = None
+    op = make_opts(x_tile, split, fallback, tau, descale, fallback_tiles)
+    rc = tos_attn_fwd(q, k, v, o, lse, B, H, N, d, causal, scale, _DTYPE_CODES[dtype], op,
+                      stream)
+    if rc != TOS_OK:
+        raise TosError(rc)
+    return o, lse

@@ -1,0 +1,164 @@
+// tos_api.hip -- the C ABI of libtos.so (declared in include/tos.h): argument
+// validation, kernel selection and launch on the caller's stream.
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "launch.hpp"
+#include "tos.h"
+
+namespace {
+
+constexpr double kLog2e = 1.4426950408889634073599246810018921;
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (a == nullptr || b == nullptr || na == 0 || nb == 0) return false;
+  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + nb && b0 < a0 + na;
+}
+
+bool aligned(const void* p, uintptr_t n) { return ((uintptr_t)p % n) == 0; }
+
+// TOS_LOG=1 in the environment prints the chosen kernel and HIP errors to stderr
+bool log_enabled() {
+  static const bool on = [] {
+    const char* e = std::getenv("TOS_LOG");
+    return e != nullptr && e[0] != '\0' && e[0] != '0';
+  }();
+  return on;
+}
+
+size_t in_elem_bytes(tos_dtype dt) { return dt == TOS_F32 ? 4 : (dt == TOS_BF16 ? 2 : 1); }
+size_t out_elem_bytes(tos_dtype dt) { return dt == TOS_F32 ? 4 : 2; }
+
+}  // namespace
+
+extern "C" {
+
+int tos_version(void) { return TOS_VERSION; }
+
+const char* tos_status_string(tos_status s) {
+  switch (s) {
+    case TOS_OK: return "TOS_OK";
+    case TOS_ERR_INVALID_ARG: return "TOS_ERR_INVALID_ARG";
+    case TOS_ERR_UNSUPPORTED: return "TOS_ERR_UNSUPPORTED";
+    case TOS_ERR_HIP: return "TOS_ERR_HIP";
+  }
+  return "TOS_UNKNOWN_STATUS";
+}
+
+double tos_attn_fwd_flops(int64_t B, int64_t H, int64_t N, int64_t d, int causal) {
+  if (B <= 0 || H <= 0 || N <= 0 || d <= 0) return 0.0;
+  const double f = 4.0 * (double)B * (double)H * (double)N * (double)N * (double)d;
+  return causal ? 0.5 * f : f;
+}
+
+tos_status tos_fwd_opts_default(tos_fwd_opts* opts) {
+  if (opts == nullptr) return TOS_ERR_INVALID_ARG;
+  std::memset(opts, 0, sizeof(*opts));
+  opts->size = (int)sizeof(tos_fwd_opts);
+  opts->x_tile = 32;
+  opts->softmax_split = TOS_SPLIT_VALU;
+  opts->fallback = TOS_FALLBACK_OFF;
+  opts->fallback_tau = 0.0f;
+  opts->q_descale = opts->k_descale = opts->v_descale = 1.0f;
+  opts->fallback_tiles = nullptr;
+  return TOS_OK;
+}
+
+tos_status tos_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
+                        tos_dtype dtype, const tos_fwd_opts* opts, void* stream) {
+  // ---- options
+  tos_fwd_opts op;
+  tos_fwd_opts_default(&op);
+  if (opts != nullptr) {
+    if (opts->size != (int)sizeof(tos_fwd_opts)) return TOS_ERR_INVALID_ARG;
+    op = *opts;
+    if (op.x_tile == 0) op.x_tile = 32;
+  }
+  if (op.x_tile != 1 && op.x_tile != 16 && op.x_tile != 32) return TOS_ERR_INVALID_ARG;
+  if (op.softmax_split != TOS_SPLIT_VALU && op.softmax_split != TOS_SPLIT_ROWSUM_MFMA)
+    return TOS_ERR_INVALID_ARG;
+  if (op.fallback != TOS_FALLBACK_OFF && op.fallback != TOS_FALLBACK_AUTO &&
+      op.fallback != TOS_FALLBACK_FORCE)
+    return TOS_ERR_INVALID_ARG;
+  if (!std::isfinite(op.fallback_tau) || op.fallback_tau < 0.0f) return TOS_ERR_INVALID_ARG;
+
+  // ---- sizes and scalars
+  if (dtype != TOS_F32 && dtype != TOS_BF16 && dtype != TOS_FP8_E4M3) return TOS_ERR_INVALID_ARG;
+  if (B < 0 || H < 0 || N < 0 || d < 0) return TOS_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return TOS_ERR_INVALID_ARG;
+  if (!std::isfinite(scale) || !(scale > 0.0f)) return TOS_ERR_INVALID_ARG;
+  if (dtype == TOS_FP8_E4M3) {
+    for (float s : {op.q_descale, op.k_descale, op.v_descale})
+      if (!std::isfinite(s) || !(s > 0.0f)) return TOS_ERR_INVALID_ARG;
+  }
+  if (B == 0 || H == 0 || N == 0) return TOS_OK;   // nothing to compute
+  if (d != 64 && d != 128) return TOS_ERR_UNSUPPORTED;
+  const int64_t BH = B * H;
+  const int64_t nqb = (N + tos::kBr - 1) / tos::kBr;
+  if (B > INT32_MAX || H > INT32_MAX || BH > INT32_MAX || N > INT32_MAX ||
+      BH * nqb > INT32_MAX)
+    return TOS_ERR_UNSUPPORTED;
+
+  // ---- pointers: required, aligned, output not overlapping anything
+  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr) return TOS_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(lse, 4))
+    return TOS_ERR_INVALID_ARG;
+  const size_t n_elem = (size_t)BH * (size_t)N * (size_t)d;
+  const size_t in_b = n_elem * in_elem_bytes(dtype), out_b = n_elem * out_elem_bytes(dtype);
+  const size_t lse_b = lse ? (size_t)BH * (size_t)N * sizeof(float) : 0;
+  for (const void* in : {q, k, v}) {
+    if (overlaps(o, out_b, in, in_b)) return TOS_ERR_INVALID_ARG;
+    if (overlaps(lse, lse_b, in, in_b)) return TOS_ERR_INVALID_ARG;
+  }
+  if (overlaps(o, out_b, lse, lse_b)) return TOS_ERR_INVALID_ARG;
+
+  // ---- kernel choice
+  tos::KernelChoice kc;
+  kc.d = (int)d;
+  kc.causal = causal != 0;
+  kc.rowsum_mfma = op.softmax_split == TOS_SPLIT_ROWSUM_MFMA;
+  kc.x = op.fallback == TOS_FALLBACK_FORCE ? 1 : op.x_tile;
+  kc.fb_auto = op.fallback == TOS_FALLBACK_AUTO && op.x_tile > 1;
+  if (dtype == TOS_F32 && kc.rowsum_mfma) return TOS_ERR_UNSUPPORTED;
+  if (dtype == TOS_FP8_E4M3) return TOS_ERR_UNSUPPORTED;
+
+  tos::FwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.BH = (int)BH;
+  a.N = (int)N;
+  a.nqb = (int)nqb;
+  a.lse_scale = scale;
+  a.c = (float)((double)scale * kLog2e);
+  a.o_scale = 1.0f;
+  a.tau = op.fallback_tau > 0.0f ? op.fallback_tau : 100.0f;
+  a.fallback_tiles = op.fallback_tiles;
+  // FORCE runs the per-row kernel and counts every X-row tile of the request
+  a.count_x = op.fallback == TOS_FALLBACK_FORCE ? op.x_tile : 0;
+  if (op.fallback == TOS_FALLBACK_AUTO && op.x_tile == 1) a.count_x = 0;
+
+  const hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipErrorNotSupported;
+  if (dtype == TOS_BF16)
+    e = tos::launch_bf16(a, kc, s);
+  else if (dtype == TOS_F32)
+    e = tos::launch_f32(a, kc, s);
+  if (log_enabled())
+    std::fprintf(stderr, "[tos] dtype=%d B=%lld H=%lld N=%lld d=%d causal=%d X=%d rowsum_mfma=%d "
+                 "fallback=%d grid=%lld: %s\n", (int)dtype, (long long)B, (long long)H,
+                 (long long)N, kc.d, (int)kc.causal, kc.x, (int)kc.rowsum_mfma, op.fallback,
+                 (long long)(BH * nqb), hipGetErrorString(e));
+  if (e == hipErrorNotSupported) return TOS_ERR_UNSUPPORTED;
+  return e == hipSuccess ? TOS_OK : TOS_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,118 @@
+"""HIP path vs the fp64 oracle, element by element, through the C ABI (GPU).
+
+Small problems run in full against oracle_attn_exact: several 128-row query
+blocks, several 64-key blocks and ragged tails.  Full-size workloads run in the
+launch configuration the benchmark times, and are checked on sampled rows the
+oracle computes one by one."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import os, sys
+sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+from parity_util import (TOL_O, assert_close, oracle_exact, real_inputs, run_gpu,
+                         sample_rows, to_device)
+from tensorized_online_softmax_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _inp(B, H, N, d, dtype, seed, std=1.0):
+    return inputs.make(B, H, N, d, dtype, seed, std=std)
+
+
+SMALL_N = [1, 17, 64, 100, 130, 257, 383]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", SMALL_N)
+def test_small_full(dtype, d, causal, N):
+    inp = _inp(2, 3, N, d, dtype, seed=100 + N + d)
+    o_ref, lse_ref = oracle_exact(inp, causal)
+    o, lse, _ = run_gpu(inp, causal)
+    assert_close(o.reshape(o_ref.shape), o_ref, lse.reshape(lse_ref.shape), lse_ref, dtype,
+                 f"{dtype} d={d} causal={causal} N={N}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("x_tile", [1, 16, 32])
+@pytest.mark.parametrize("split", ["valu", "rowsum_mfma"])
+@pytest.mark.parametrize("fallback", ["off", "auto", "force"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_knobs(dtype, x_tile, split, fallback, causal):
+    if dtype == "f32" and split == "rowsum_mfma":
+        pytest.skip("row sum on the matrix unit is a bf16 option")
+    inp = _inp(1, 4, 300, 64, dtype, seed=7)
+    o_ref, lse_ref = oracle_exact(inp, causal)
+    o, lse, tiles = run_gpu(inp, causal, x_tile=x_tile, split=split, fallback=fallback,
+                            counter=True)
+    assert_close(o.reshape(o_ref.shape), o_ref, lse.reshape(lse_ref.shape), lse_ref, dtype,
+                 f"{dtype} X={x_tile} {split} fallback={fallback} causal={causal}")
+    ntile = 4 * math.ceil(300 / x_tile)
+    if fallback == "force":
+        assert tiles == ntile
+    else:
+        assert tiles == 0   # N(0,1) inputs never come near the threshold
+
+
+def test_fallback_auto_switches_on_spiky_rows():
+    """Spiky rows next to flat rows with a low threshold: AUTO switches tiles to
+    per-row maxima and still matches; OFF and AUTO agree with the oracle."""
+    N, d = 512, 128
+    inp = inputs.make(1, 2, N, d, "bf16", seed=55, std=math.sqrt(8.0), spike_frac=0.2,
+                      spike_logit=40.0)
+    o_ref, lse_ref = oracle_exact(inp, False)
+    for fb, tau in (("off", 0.0), ("auto", 12.0), ("auto", 0.0)):
+        o, lse, tiles = run_gpu(inp, False, fallback=fb, tau=tau, counter=True)
+        assert_close(o.reshape(o_ref.shape), o_ref, lse.reshape(lse_ref.shape), lse_ref,
+                     "bf16", f"spiky fallback={fb} tau={tau}", storage_ulp=True)
+        if fb == "auto" and tau == 12.0:
+            assert tiles > 0
+        if fb == "off" or tau == 0.0:
+            assert tiles == 0   # default tau (100) is far above these gaps
+
+
+def test_deterministic():
+    inp = _inp(2, 4, 1000, 128, "bf16", seed=9)
+    dev = to_device(inp)
+    o1, l1, _ = run_gpu(inp, True, dev=dev)
+    o2, l2, _ = run_gpu(inp, True, dev=dev)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_one_hot_v_rows_sum_to_one():
+    """V = identity (d = N = 64): O holds the probabilities; rows sum to 1 and
+    masked entries are 0."""
+    N = d = 64
+    inp = _inp(1, 2, N, d, "f32", seed=21, std=2.0)
+    inp["v"] = torch.eye(N, dtype=torch.float32).expand(1, 2, N, N).contiguous()
+    for causal in (False, True):
+        o, _, _ = run_gpu(inp, causal)
+        o = o.reshape(2, N, N)
+        assert np.abs(o.sum(-1) - 1.0).max() <= 1e-5
+        assert o.min() >= 0.0
+        if causal:
+            assert np.all(np.triu(o, 1) == 0.0)
+
+
+@pytest.mark.parametrize("name", ["single_head_f32", "mha_bf16", "causal_bf16",
+                                  "long_causal_bf16"])
+def test_workload_sampled(name):
+    w = inputs.WORKLOADS[name]
+    inp = inputs.make_workload(w)
+    o, lse, _ = run_gpu(inp, w.causal, x_tile=w.x_tile)
+    BH = w.B * w.H
+    o = o.reshape(BH * w.N, w.d)
+    lse = lse.reshape(BH * w.N)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    if BH * w.N <= 200000 and w.N <= 1024:
+        o_ref, lse_ref = oracle_exact(inp, w.causal)
+        assert_close(o, o_ref.reshape(o.shape), lse, lse_ref.reshape(lse.shape), w.dtype, name)
+    else:
+        rows = sample_rows(BH, w.N, 384, seed=w.seed, causal=w.causal)
+        o_ref, lse_ref = oracle_exact(inp, w.causal, rows=rows)
+        assert_close(o[rows], o_ref, lse[rows], lse_ref, w.dtype, name)
