@@ -1,0 +1,190 @@
+"""Throughput of the fused attention forward pass (tensorized online softmax) on
+one MI355X, as one JSON line.
+
+A step is one call of tos_attn_fwd over the whole workload (all key blocks, the
+softmax, both products, the epilogue) with inputs already resident in HBM.
+Default workload: causal bf16 attention, B=2, H=32, N=4096, d=128 (X = 32).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--split valu|rowsum_mfma] [--x-tile X] [--no-cpu-baseline]
+                    [--copy-calib-mib M]
+
+--copy-calib-mib M also runs one plain device-to-device copy of M MiB after the
+timed region; rocprofv3 counter runs of this command use it to calibrate the
+FETCH_SIZE / WRITE_SIZE counters against a kernel of known traffic.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"bf16": 2516.6, "fp8": 5033.2, "f32": 157.3}   # MI355X dense MFMA
+HBM_GBPS = 8000.0
+KERNEL_SOURCES = ["tensorized_online_softmax_amd/csrc/attn_fwd_kernels.hpp",
+                  "tensorized_online_softmax_amd/csrc/softmax_tile.hpp"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_{workload}.txt")
+
+
+def kernel_hash():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload):
+    """HBM bytes per launch from the committed counter summary, or None when
+    there is none or the kernel sources changed since it was taken."""
+    path = TRAFFIC_FILE.format(workload=workload)
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_sources_sha256_16") != kernel_hash():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, inp, target_rows):
+    """The fp64 oracle (exact attention) on a seeded sample of the workload's
+    rows, on every host core this process may use."""
+    import numpy as np
+    import oracle
+    from tensorized_online_softmax_amd import inputs
+    threads = min(len(os.sched_getaffinity(0)),
+                  int(os.environ.get("OMP_NUM_THREADS", "0")) or 1 << 30)
+    q, k, v = (inputs.real_values(inp[n], inp["descale"][n]) for n in ("q", "k", "v"))
+    BH = w.B * w.H
+    if target_rows <= 0 or target_rows >= BH * w.N:
+        target_rows = BH * w.N
+        rows = np.arange(BH * w.N, dtype=np.int64)
+    else:
+        rows = np.sort(np.random.default_rng(w.seed + 99).choice(BH * w.N, size=target_rows,
+                                                                  replace=False))
+    i = rows % w.N
+    keys = (i + 1) if w.causal else np.full(rows.shape, w.N)
+    flops = float(np.sum(4.0 * w.d * keys))
+    t0 = time.perf_counter()
+    oracle.attn_exact(q, k, v, w.causal, w.scale, rows=rows, threads=threads)
+    dt = time.perf_counter() - t0
+    what = ("every query row" if target_rows == BH * w.N
+            else f"{target_rows} of {BH * w.N} query rows (seeded uniform)")
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{what} of the workload, each over its full key range; fp64 exact "
+                      f"attention (oracle_attn_exact), {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="causal_bf16")
+    ap.add_argument("--split", default="valu", choices=["valu", "rowsum_mfma"])
+    ap.add_argument("--x-tile", type=int, default=None)
+    ap.add_argument("--fallback", default="off", choices=["off", "auto", "force"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=0, help="0 = every row")
+    ap.add_argument("--copy-calib-mib", type=int, default=0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(heads shard across GPUs with no exchange; see the design notes). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from tensorized_online_softmax_amd import binding, inputs
+
+    w = inputs.WORKLOADS[args.workload]
+    x_tile = args.x_tile or w.x_tile
+    print(f"[bench] workload {w.name}: B={w.B} H={w.H} N={w.N} d={w.d} {w.dtype} "
+          f"causal={w.causal} X={x_tile} split={args.split}", file=sys.stderr, flush=True)
+    inp = inputs.make_workload(w)
+    torch.cuda.set_device(0)
+    q, k, v = (inp[n].cuda() for n in ("q", "k", "v"))
+    odt = torch.float32 if w.dtype == "f32" else torch.bfloat16
+    o = torch.empty((w.B, w.H, w.N, w.d), dtype=odt, device="cuda")
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
+    descale = inp["descale"] if w.dtype == "fp8" else None
+
+    def step():
+        binding.attn_fwd(q, k, v, causal=w.causal, scale=w.scale, dtype=w.dtype,
+                         x_tile=x_tile, split=args.split, fallback=args.fallback,
+                         descale=descale, out=o, lse=lse)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()   # the stream the kernels are launched on
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    avg_launch_s = sum(launch_ms) / len(launch_ms) / 1e3
+    ms_per_step = wall * 1e3 / args.steps
+    flops = w.flops()
+    print(f"[bench] {args.steps} steps in {wall:.3f} s; launch avg {avg_launch_s * 1e6:.1f} us "
+          f"min {min(launch_ms) * 1e3:.1f} us max {max(launch_ms) * 1e3:.1f} us",
+          file=sys.stderr, flush=True)
+
+    if args.copy_calib_mib > 0:
+        n = args.copy_calib_mib * 1024 * 1024 // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] calibration copy: {args.copy_calib_mib} MiB read + written",
+              file=sys.stderr, flush=True)
+
+    peak = PEAK_TFLOPS[w.dtype]
+    achieved = flops / avg_launch_s / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": read_traffic(w.name)}
+    result = {
+        "metric": "fused attention fwd TFLOP/s at 1 GPU and % of MFMA peak (bf16, fp8)",
+        "value": round(flops / (ms_per_step / 1e3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) inputs, numpy PCG64)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                   "causal": w.causal, "x_tile": x_tile, "softmax_split": args.split,
+                   "fallback": args.fallback, "Br": 128, "Bc": 64,
+                   "flops_per_step": flops, "pct_of_peak": round(100 * achieved / peak, 2)},
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_rows)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
