@@ -177,7 +177,7 @@ def main():
         "data": "synthetic (seeded N(0,1) inputs, numpy PCG64)",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
                    "causal": w.causal, "x_tile": x_tile, "softmax_split": args.split,
-                   "fallback": args.fallback, "Br": 128, "Bc": 64,
+                   "fallback": args.fallback, "Br": 128 if w.dtype == "f32" else 256, "Bc": 64,
                    "flops_per_step": flops, "pct_of_peak": round(100 * achieved / peak, 2)},
         "roofline": roofline,
     }

@@ -44,7 +44,7 @@ struct FwdArgs {
   float* lse;
   int BH;            // batch * heads
   int N;             // sequence length
-  int nqb;           // query blocks per head = ceil(N / 128)
+  int nqb;           // query blocks per head (set by the launcher for its block size)
   float c;           // scale * log2(e) (fp8: times the q and k descales)
   float lse_scale;   // scale (fp8: times the q and k descales)
   float o_scale;     // multiplies O at the end (fp8: the v descale)
@@ -81,40 +81,103 @@ __device__ __forceinline__ void count_tiles(const FwdArgs& a, const RowState& st
 }
 
 // ---------------------------------------------------------------------------
-// bf16: v_mfma_f32_32x32x16_bf16 for both products.
+// bf16: v_mfma_f32_32x32x16_bf16 for both products, software-pipelined.
+//
+// A workgroup has 8 waves = 256 query rows (waves w and w+4 share a SIMD) and
+// one LDS ring of key blocks.  Each wave runs its own three-stage pipeline: in
+// the step for key block j it issues, in one instruction stream,
+//   matrix unit : O^T += V_{j-1}^T P~_{j-1}^T   and   S_{j+1} = K_{j+1} Q^T
+//   vector units: the softmax of S_j -> P~_j (tile max, exp2, pack, row sums)
+// with the MFMAs spread evenly between the vector instructions, so that the
+// tensor and vector work of FlashAttention-T (section A2, tensor-vector
+// scheduling) overlap inside the wave, and the second wave on the SIMD fills
+// what one wave leaves idle.  The rescale of O by alpha_j (rare: the surrogate
+// maximum seldom moves) waits until the P~_{j-1} product is in O.
+//
+// Key blocks stream into LDS rings (4 slots for K, 3 for V) through buffer
+// loads that write LDS directly (no registers; rows past N read as 0).  Step j
+// issues K_{j+3} and V_{j+1}, two steps before their first reads; each
+// overwrites a slot last read two steps earlier.  Every step ends with a plain
+// barrier after waiting until only the loads issued in that step are in
+// flight.  A direct-to-LDS load writes 1 KiB per wave instruction,
+// contiguous, so rows are not padded: 16-byte chunks are XOR-swizzled within
+// each row instead, which keeps the K operand reads (16 rows, one chunk each)
+// and the transposing V reads (4 rows x 2 chunks per 16 lanes) free of LDS bank
+// conflicts.
 // ---------------------------------------------------------------------------
+constexpr int kPWaves = 8;
+constexpr int kPThreads = 64 * kPWaves;
+constexpr int kPBr = 32 * kPWaves;   // 256 query rows per workgroup
+constexpr int kKSlots = 4;           // LDS ring slots for K
+constexpr int kVSlots = 3;           // LDS ring slots for V
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned bytes) {
+  // raw buffer: stride 0, num_records = bytes; reads past the end return 0
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+// LDS position (16-byte chunk index within the row) of chunk c of row r
+template <int D> __device__ __forceinline__ int kswz(int r, int c) {
+  return D == 128 ? (c ^ (r & 15)) : (c ^ ((r >> 1) & 7));
+}
+template <int D> __device__ __forceinline__ int vswz(int r, int c) {
+  return D == 128 ? (c ^ (4 * (r & 3))) : (c ^ (4 * ((r >> 1) & 1)));
+}
+
+// NW direct-to-LDS loads of 1 KiB each: instruction k writes LDS bytes
+// [dst + 1024k, +1024) (16 bytes per lane, in lane order) from the byte offsets
+// goff[k] + base of the buffer.  A plain device function: the builtin exists
+// only for the device, and kernel lambdas are compiled for the host as well.
+template <int NW>
+__device__ __forceinline__ void dma_block(__amdgpu_buffer_rsrc_t rs, char* dst, const unsigned* goff,
+                                          unsigned base) {
+#pragma unroll
+  for (int k = 0; k < NW; ++k)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rs, (__attribute__((address_space(3))) void*)(dst + 1024 * k), 16, goff[k] + base, 0, 0, 0);
+}
+
+// end of a step: wait until at most NV vector-memory loads of this wave are in
+// flight and its LDS reads are done, then the workgroup barrier.  The memory
+// clobber keeps the compiler from moving LDS accesses across it.
+template <int NV> __device__ __forceinline__ void step_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(NV) : "memory");
+}
+
 template <int D, bool CAUSAL, int X, bool ROWSUM_MFMA, bool FB_AUTO>
-__global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16(FwdArgs a) {
+__global__ __launch_bounds__(kPThreads, 1) void attn_fwd_bf16(FwdArgs a) {
   static_assert(D == 64 || D == 128, "head dim");
-  constexpr int KS = D + 8;    // K row stride in LDS (elements): rows 4 banks apart
-  constexpr int VS = D + 32;   // V row stride: transposing reads hit 4 rows x 32 B
-  constexpr int CH = kBc * D / 8 / kThreads;   // 16-byte chunks per thread per tensor
+  constexpr int RB = 2 * D;                 // bytes per K or V row
+  constexpr int BLK = kBc * RB;             // bytes per key block of K or V
+  constexpr int CHW = BLK / 1024 / kPWaves;   // 1 KiB load instructions per wave per tensor
   constexpr int NKK = D / 16;  // k-steps of S^T = K Q^T
   constexpr int NMT = D / 32;  // 32-row M tiles of O^T
-  __shared__ __attribute__((aligned(16))) __bf16 smem[2 * kBc * KS + 2 * kBc * VS];
-  __bf16* kl = smem;
-  __bf16* vl = smem + 2 * kBc * KS;
+  __shared__ __attribute__((aligned(1024))) char smem[(kKSlots + kVSlots) * BLK];
+  char* kring = smem;
+  char* vring = smem + kKSlots * BLK;
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, ln = lane & 31, hf = lane >> 5;
-  int bh, q0;
-  block_coords(a, CAUSAL, bh, q0);
+  const int bid = blockIdx.x;
+  const int bh = bid % a.BH;
+  const int qb = CAUSAL ? (a.nqb - 1 - bid / a.BH) : bid / a.BH;
+  const int q0 = qb * kPBr;
   const int N = a.N;
   const int qrow = q0 + 32 * w + ln;
   const bool qvalid = qrow < N;
   const size_t head = (size_t)bh * N * D;
   const __bf16* Q = (const __bf16*)a.q + head;
-  const __bf16* K = (const __bf16*)a.k + head;
-  const __bf16* V = (const __bf16*)a.v + head;
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc((const __bf16*)a.k + head, (unsigned)N * RB);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc((const __bf16*)a.v + head, (unsigned)N * RB);
 
   // key blocks: all of them, or (causal) up to the workgroup's last query
   const int nblk = (N + kBc - 1) / kBc;
-  const int qlast_wg = min(q0 + kBr, N) - 1;
+  const int qlast_wg = min(q0 + kPBr, N) - 1;
   const int jend = CAUSAL ? qlast_wg / kBc + 1 : nblk;
   const int wq0 = q0 + 32 * w;                       // first query of the wave
   const int wqlast = min(wq0 + 31, N - 1);
   const int jend_w = (wq0 >= N) ? 0 : (CAUSAL ? wqlast / kBc + 1 : nblk);
-  // keys this lane may see: [0, klim)
-  const int klim = qvalid ? (CAUSAL ? qrow + 1 : N) : 0;
+  const int klim = qvalid ? (CAUSAL ? qrow + 1 : N) : 0;   // keys this lane may see
 
   // Q^T operand: lane (query ln, half hf) holds Q[qrow][16 kk + 8 hf + 0..7]
   bf16x8 qf[NKK];
@@ -126,29 +189,37 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16(FwdArgs a) {
       qf[kk] = bf16x8{};
   }
 
-  u32x4 kreg[CH], vreg[CH];
-  auto gload = [&](int j) {
-    const int kb = j * kBc;
+  // direct-to-LDS loads: instruction k of this wave fills LDS bytes
+  // [(w*CHW + k)*1024, +1024) of the slot, lane L the 16 bytes at +16L, i.e.
+  // row r, chunk position p; it fetches chunk c = p xor swizzle(r) of row r
+  unsigned kgoff[CHW], vgoff[CHW];
 #pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int c = tid + kThreads * i, row = c / (D / 8), col = (c % (D / 8)) * 8;
-      if (kb + row < N) {
-        kreg[i] = *(const u32x4*)(K + (size_t)(kb + row) * D + col);
-        vreg[i] = *(const u32x4*)(V + (size_t)(kb + row) * D + col);
-      } else {
-        kreg[i] = u32x4{0, 0, 0, 0};   // keys past N: zero K (masked) and zero V
-        vreg[i] = u32x4{0, 0, 0, 0};
-      }
-    }
+  for (int k = 0; k < CHW; ++k) {
+    const int L = (w * CHW + k) * 1024 + 16 * lane, r = L / RB, p = (L % RB) / 16;
+    kgoff[k] = (unsigned)(r * RB + 16 * kswz<D>(r, p));
+    vgoff[k] = (unsigned)(r * RB + 16 * vswz<D>(r, p));
+  }
+  auto load_k = [&](int j) {
+    dma_block<CHW>(krs, kring + (j % kKSlots) * BLK + w * CHW * 1024, kgoff, (unsigned)j * BLK);
   };
-  auto lstore = [&](int buf) {
+  auto load_v = [&](int j) {
+    dma_block<CHW>(vrs, vring + (j % kVSlots) * BLK + w * CHW * 1024, vgoff, (unsigned)j * BLK);
+  };
+
+  // K operand reads: lane (key ln of tile t, half hf) reads chunk 2kk + hf of
+  // row 32t + ln; the swizzle depends on the row only through ln
+  int koff[NKK];
 #pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int c = tid + kThreads * i, row = c / (D / 8), col = (c % (D / 8)) * 8;
-      *(u32x4*)(kl + buf * kBc * KS + row * KS + col) = kreg[i];
-      *(u32x4*)(vl + buf * kBc * VS + row * VS + col) = vreg[i];
-    }
-  };
+  for (int kk = 0; kk < NKK; ++kk) koff[kk] = ln * RB + 16 * kswz<D>(ln, 2 * kk + hf);
+  // V transposing reads: lane (16-lane group G, index i) reads 8 bytes of row
+  // 16s + 4(G/2) + i/4 (+8 for slots 4..7) at element 32mt + 16(G%2) + 4(i%4),
+  // i.e. chunk 4mt + 2(G%2) + (i%4)/2, byte 8((i%4)%2) within it
+  const int G = lane >> 4, gi = lane & 15;
+  const int vr0 = 4 * (G >> 1) + (gi >> 2);
+  int voff[NMT];
+#pragma unroll
+  for (int mt = 0; mt < NMT; ++mt)
+    voff[mt] = vr0 * RB + 16 * vswz<D>(vr0, 4 * mt + 2 * (G & 1) + ((gi & 3) >> 1)) + 8 * (gi & 1);
 
   RowState st;
   row_state_init(st, X == 1);
@@ -164,113 +235,168 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16(FwdArgs a) {
   for (int t = 0; t < 8; ++t) ones[t] = (__bf16)1.0f;
   const bf16x2 ones2 = {(__bf16)1.0f, (__bf16)1.0f};
 
-  if (jend > 0) {
-    gload(0);
-    lstore(0);
-  }
-  __syncthreads();
-
-  for (int j = 0; j < jend; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < jend) gload(j + 1);
-    if (j < jend_w) {
-      const __bf16* kt = kl + buf * kBc * KS;
-      const __bf16* vt = vl + buf * kBc * VS;
-      // ---- S^T = K_j Q^T: two 32-key tiles
-      f32x16 s0 = {}, s1 = {};
+  // S^T = K_j Q^T into (t0, t1), two 32-key tiles
+  auto qk = [&](int j, f32x16& t0, f32x16& t1) {
+    const char* kt = kring + (j % kKSlots) * BLK;
+    t0 = f32x16{};
+    t1 = f32x16{};
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        const bf16x8 a0 = *(const bf16x8*)(kt + ln * KS + 16 * kk + 8 * hf);
-        const bf16x8 a1 = *(const bf16x8*)(kt + (32 + ln) * KS + 16 * kk + 8 * hf);
-        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[kk], s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[kk], s1, 0, 0, 0);
+    for (int kk = 0; kk < NKK; ++kk) {
+      const bf16x8 a0 = *(const bf16x8*)(kt + koff[kk]);
+      const bf16x8 a1 = *(const bf16x8*)(kt + koff[kk] + 32 * RB);
+      t0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[kk], t0, 0, 0, 0);
+      t1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[kk], t1, 0, 0, 0);
+    }
+  };
+  // O^T += V_j^T P~^T, 16 keys per step.  Step s, slot t of lane half h is
+  // key 16s + 8(t/4) + 4h + t%4 (the accumulator order of S^T), which the
+  // transposing reads above fetch.
+  auto pv = [&](int j, const bf16x8* pk) {
+    const char* vt = vring + (j % kVSlots) * BLK;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt) {
+        const char* p = vt + voff[mt] + 16 * s * RB;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(p));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(p + 8 * RB));
+        const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        oacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pk[s], oacc[mt], 0, 0, 0);
       }
-      // ---- mask: key index of register r of tile t is kb + 32t + 8(r/4) + 4hf + r%4
+      if constexpr (ROWSUM_MFMA)   // step 7 on the matrix unit: ones x P~^T
+        lacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pk[s], lacc, 0, 0, 0);
+    }
+  };
+  // Steps 1-7 of Algorithm 1 for key block j: logits (s0, s1) -> P~ in pk.
+  // The vector row sums absorb alpha at once; the returned alpha still has to
+  // be applied to the matrix accumulators (O, and l on the MFMA) once the
+  // previous block's P~V product has landed in them.
+  auto softmax = [&](int j, f32x16& s0, f32x16& s1, bf16x8* pk, bool masked) -> float {
+    if (masked) {
+      // only a wave's last block can hold keys past the diagonal or past N:
+      // key of register r of tile t is kb + 32t + 8(r/4) + 4hf + r%4
       const int kb = j * kBc;
-      const bool need_mask = (kb + kBc > N) || (wq0 + 32 > N) || (CAUSAL && kb + kBc > wq0 + 1);
-      if (need_mask) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kb + 8 * (r / 4) + 4 * hf + (r % 4);
-          if (key >= klim) s0[r] = -__builtin_inff();
-          if (key + 32 >= klim) s1[r] = -__builtin_inff();
-        }
-      }
-      // ---- Algorithm 1 step 1 and the reference update (steps 2-3)
-      float bm = s0[0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) bm = fmax_raw(bm, s0[r]);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) bm = fmax_raw(bm, s1[r]);
-      const float alpha = row_state_update<X, FB_AUTO>(st, bm, c, tau);
-      // uniform over the tile; the whole wave skips the rescale when no row's
-      // reference moved (alpha == 1 everywhere)
-      if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
-#pragma unroll
-        for (int mt = 0; mt < NMT; ++mt) oacc[mt] *= alpha;
-        if constexpr (ROWSUM_MFMA)
-          lacc *= alpha;
-        else
-          lsum *= alpha;
-        lexact *= alpha;
-      }
-      // ---- steps 4-6: P~ = exp2(c*S - c*ref), packed to bf16 as the B operand
-      const float nb = neg_c_ref(st, c);
-      bf16x8 pk[4];
-      float pe0 = 0.0f, pe1 = 0.0f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], c, nb));
-        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], c, nb));
-        pe0 += p0;
-        pe1 += p1;
-        pk[r / 8][r % 8] = (__bf16)p0;
-        pk[2 + r / 8][r % 8] = (__bf16)p1;
-      }
-      // two row sums (step 7): the unrounded one gives lse; the one over the
-      // rounded P~ the P~V product consumes normalises O, so O / l stays a
-      // weighted average of V rows (bf16 rounding of P~ then cancels to first
-      // order instead of adding to the error of O)
-      lexact += pe0 + pe1;
-      if constexpr (!ROWSUM_MFMA) {
-        // on the vector unit: dot products of each packed pair with (1, 1)
-        float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          ps[0] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pk[s], pk[s], 0, 1), ones2, ps[0], false);
-          ps[1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pk[s], pk[s], 2, 3), ones2, ps[1], false);
-          ps[2] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pk[s], pk[s], 4, 5), ones2, ps[2], false);
-          ps[3] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pk[s], pk[s], 6, 7), ones2, ps[3], false);
-        }
-        lsum += (ps[0] + ps[1]) + (ps[2] + ps[3]);
-      }
-      // ---- O^T += V_j^T P~^T, 16 keys per step.  Step s, slot t of lane half h
-      // is key 16s + 8(t/4) + 4h + t%4 (the accumulator order above); the
-      // transposing read gives lane (16-lane group G, index i) the V row
-      // 16s + 4(G/2) + i/4 (+8 for slots 4..7) at columns 16(G%2) + 4(i%4).
-      const int G = lane >> 4, gi = lane & 15;
-      const int vrow = 4 * (G >> 1) + (gi >> 2);
-      const int vcol = 16 * (G & 1) + 4 * (gi & 3);
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-#pragma unroll
-        for (int mt = 0; mt < NMT; ++mt) {
-          const __bf16* p = vt + (16 * s + vrow) * VS + 32 * mt + vcol;
-          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4*)(p));
-          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4*)(p + 8 * VS));
-          const i16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          const bf16x8 av = __builtin_bit_cast(bf16x8, both);
-          oacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pk[s], oacc[mt], 0, 0, 0);
-        }
-        if constexpr (ROWSUM_MFMA)   // step 7 on the matrix unit: ones x P~^T
-          lacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pk[s], lacc, 0, 0, 0);
+        const int key = kb + 8 * (r / 4) + 4 * hf + (r % 4);
+        if (key >= klim) s0[r] = -__builtin_inff();
+        if (key + 32 >= klim) s1[r] = -__builtin_inff();
       }
     }
-    if (j + 1 < jend) lstore((j + 1) & 1);
-    __syncthreads();
+    // step 1 and the reference update (steps 2-3); rows past N stay out of the
+    // tile maximum
+    float bm = fmax_raw(s0[0], s0[1]);
+#pragma unroll
+    for (int r = 2; r < 16; ++r) bm = fmax_raw(bm, s0[r]);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) bm = fmax_raw(bm, s1[r]);
+    bm = qvalid ? bm : -__builtin_inff();
+    const float alpha = row_state_update<X, FB_AUTO>(st, bm, c, tau);
+    // steps 4-6: P~ = exp2(c*S - c*ref), packed to bf16 as the B operand
+    const float nb = neg_c_ref(st, c);
+    float pe0 = 0.0f, pe1 = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], c, nb));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], c, nb));
+      pe0 += p0;
+      pe1 += p1;
+      pk[r / 8][r % 8] = (__bf16)p0;
+      pk[2 + r / 8][r % 8] = (__bf16)p1;
+    }
+    // two row sums (step 7): the unrounded one gives lse; the one over the
+    // rounded P~ the P~V product consumes normalises O, so O / l stays a
+    // weighted average of V rows (bf16 rounding of P~ then cancels to first
+    // order instead of adding to the error of O)
+    lexact = lexact * alpha + (pe0 + pe1);
+    if constexpr (!ROWSUM_MFMA) {
+      // on the vector unit: dot products of each packed pair with (1, 1)
+      float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        ps[0] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pk[s], pk[s], 0, 1), ones2, ps[0], false);
+        ps[1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pk[s], pk[s], 2, 3), ones2, ps[1], false);
+        ps[2] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pk[s], pk[s], 4, 5), ones2, ps[2], false);
+        ps[3] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pk[s], pk[s], 6, 7), ones2, ps[3], false);
+      }
+      lsum = lsum * alpha + ((ps[0] + ps[1]) + (ps[2] + ps[3]));
+    }
+    return alpha;
+  };
+  // alpha on the matrix accumulators; the whole wave skips it when no row's
+  // reference moved (alpha == 1 everywhere, the common case)
+  auto rescale = [&](float alpha) {
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt) oacc[mt] *= alpha;
+      if constexpr (ROWSUM_MFMA) lacc *= alpha;
+    }
+  };
+
+  // Loads issued in step j (K_{j+3}, V_{j+1}) and the end-of-step barrier:
+  // only the loads issued in this step may still be in flight after it.
+  auto step_loads = [&](int j) {
+    if (j + 3 < jend) load_k(j + 3);
+    if (j + 1 < jend) load_v(j + 1);
+  };
+  auto step_end = [&](int j) {
+    const int nk = (j + 3 < jend) ? CHW : 0, nv = (j + 1 < jend) ? CHW : 0;
+    if (nk + nv == 2 * CHW)
+      step_barrier<2 * CHW>();
+    else if (nk + nv == CHW)
+      step_barrier<CHW>();
+    else
+      step_barrier<0>();
+  };
+
+  // ---- prologue: K_0, K_1, K_2 and V_0 into the rings, then S_0
+  load_k(0);
+  if (jend > 1) load_k(1);
+  if (jend > 2) load_k(2);
+  load_v(0);
+  step_barrier<0>();
+  f32x16 s0 = {}, s1 = {};     // S_j, then S_{j+1} (same registers)
+  bf16x8 pp[4], pc[4];         // P~_{j-1} and P~_j
+#pragma unroll
+  for (int t = 0; t < 4; ++t) pp[t] = pc[t] = bf16x8{};
+  if (jend_w > 0) qk(0, s0, s1);
+
+  // Three phases, so that the steady loop has a single path and its loop
+  // carried registers (S, P~, O) are updated in place:
+  //   first step (j = 0), steady steps (1 <= j < jend_w - 1), then the wave's
+  //   last block, the final P~V product and the idle steps up to jend.
+  // Each step (any phase) issues its loads and ends with the barrier, so every
+  // wave passes the same jend + 1 barriers.
+  auto edge_step = [&](int j) {
+    step_loads(j);
+    if (j >= 1 && j <= jend_w) pv(j - 1, pp);
+    if (j < jend_w) {
+      const float alpha = softmax(j, s0, s1, pc, j == jend_w - 1);
+      if (j + 1 < jend_w) qk(j + 1, s0, s1);
+      rescale(alpha);
+    }
+    step_end(j);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) pp[t] = pc[t];
+  };
+  int j = 0;
+  if (jend >= 0) edge_step(j++);
+  for (; j + 1 < jend_w; ++j) {
+    // steady state, one instruction stream: P~_{j-1} V_{j-1} and the softmax
+    // of S_j, then S_{j+1} into the same registers
+    step_loads(j);
+    pv(j - 1, pp);
+    const float alpha = softmax(j, s0, s1, pc, false);
+    __builtin_amdgcn_sched_barrier(0);
+    qk(j + 1, s0, s1);
+    rescale(alpha);
+    step_end(j);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) pp[t] = pc[t];
   }
+  for (; j <= jend; ++j) edge_step(j);
 
   // ---- epilogue: l, O / l, lse (reading R-7: lse = scale*ref + ln l)
   float l;
@@ -288,7 +414,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16(FwdArgs a) {
       for (int g = 0; g < 4; ++g) {
         bf16x4 ov;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) ov[t] = (__bf16)(oacc[mt][4 * g + t] * inv);
+        for (int u = 0; u < 4; ++u) ov[u] = (__bf16)(oacc[mt][4 * g + u] * inv);
         *(bf16x4*)(O + 32 * mt + 8 * g + 4 * hf) = ov;
       }
     }

@@ -5,10 +5,11 @@ namespace tos {
 
 template <int D, bool CAUSAL, int X, bool RS, bool FB>
 static hipError_t go(const FwdArgs& a, hipStream_t s) {
-  const dim3 grid((unsigned)a.BH * (unsigned)a.nqb), block(kThreads);
+  FwdArgs arg = a;
+  arg.nqb = (a.N + kPBr - 1) / kPBr;
+  const dim3 grid((unsigned)arg.BH * (unsigned)arg.nqb), block(kPThreads);
   // hipLaunchKernel reports this launch's own status (hipGetLastError could
   // return an error left behind by an earlier, unrelated call)
-  FwdArgs arg = a;
   void* params[] = {&arg};
   return hipLaunchKernel(reinterpret_cast<const void*>(&attn_fwd_bf16<D, CAUSAL, X, RS, FB>), grid, block, params, 0, s);
 }

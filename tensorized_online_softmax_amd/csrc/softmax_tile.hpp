@@ -80,6 +80,8 @@ __device__ __forceinline__ void row_state_init(RowState& st, bool per_row) {
 // was accumulated yet, 1 when the row still has no key) and updates the state.
 template <int X, bool FB_AUTO>
 __device__ __forceinline__ float row_state_update(RowState& st, float blk_max, float c, float tau) {
+  // straight-line code (selects, no branches), so that the caller's matrix
+  // instructions can be interleaved with it in one basic block
   const float ninf = -__builtin_inff();
   st.m_run = fmax_raw(st.m_run, pair_reduce(blk_max, MaxOp()));
   float ref_new;
@@ -88,23 +90,20 @@ __device__ __forceinline__ float row_state_update(RowState& st, float blk_max, f
   } else {
     const float tm = tile_reduce<X>(st.m_run, MaxOp());
     if constexpr (FB_AUTO) {
-      if (!st.per_row) {
-        // rows without a key yet cannot underflow: leave them out of the min
-        const float mn = tile_reduce<X>(st.m_run == ninf ? __builtin_inff() : st.m_run, MinOp());
-        if (c * (tm - mn) > tau) st.per_row = true;
-      }
+      // rows without a key yet cannot underflow: leave them out of the min
+      const float mn = tile_reduce<X>(st.m_run == ninf ? __builtin_inff() : st.m_run, MinOp());
+      st.per_row = st.per_row || (c * (tm - mn) > tau);
       ref_new = st.per_row ? st.m_run : tm;
     } else {
       ref_new = tm;
     }
   }
-  float alpha;
-  if (st.ref == ninf)
-    alpha = 0.0f;
-  else if (ref_new == ninf)
-    alpha = 1.0f;
-  else
-    alpha = __builtin_amdgcn_exp2f(c * (st.ref - ref_new));
+  // alpha = exp2(c*(ref_old - ref_new)); 0 when nothing was accumulated yet,
+  // 1 when the row still has no key
+  const bool none_yet = st.ref == ninf, no_key = ref_new == ninf;
+  const float arg = (none_yet || no_key) ? 0.0f : c * (st.ref - ref_new);
+  float alpha = __builtin_amdgcn_exp2f(arg);
+  alpha = none_yet ? 0.0f : alpha;
   st.ref = ref_new;
   return alpha;
 }

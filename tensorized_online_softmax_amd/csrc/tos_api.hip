@@ -100,8 +100,9 @@ tos_status tos_attn_fwd(const void* q, const void* k, const void* v, void* o, fl
   if (d != 64 && d != 128) return TOS_ERR_UNSUPPORTED;
   const int64_t BH = B * H;
   const int64_t nqb = (N + tos::kBr - 1) / tos::kBr;
+  // grid size in 32 bits; one head of K or V addressable by a 32-bit buffer offset
   if (B > INT32_MAX || H > INT32_MAX || BH > INT32_MAX || N > INT32_MAX ||
-      BH * nqb > INT32_MAX)
+      BH * nqb > INT32_MAX || N * d * (int64_t)in_elem_bytes(dtype) > INT32_MAX)
     return TOS_ERR_UNSUPPORTED;
 
   // ---- pointers: required, aligned, output not overlapping anything
