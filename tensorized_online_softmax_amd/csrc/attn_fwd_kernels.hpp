@@ -111,10 +111,28 @@ constexpr int kPBr = 32 * kPWaves;   // 256 query rows per workgroup
 constexpr int kKSlots = 4;           // LDS ring slots for K
 constexpr int kVSlots = 3;           // LDS ring slots for V
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned bytes) {
-  // raw buffer: stride 0, num_records = bytes; reads past the end return 0
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                           0x00020000);
+// Raw buffer descriptor (stride 0) over [base, base + bytes): loads at offsets
+// at or past `bytes` return zeros.  The fourth word is the gfx9 data format
+// for untyped dword loads.
+__device__ __forceinline__ u32x4 buffer_desc(const void* base, unsigned bytes) {
+  const unsigned long long b = (unsigned long long)base;
+  u32x4 d;
+  d[0] = __builtin_amdgcn_readfirstlane((unsigned)b);
+  d[1] = __builtin_amdgcn_readfirstlane((unsigned)(b >> 32) & 0xffffu);
+  d[2] = __builtin_amdgcn_readfirstlane(bytes);
+  d[3] = 0x00020000u;
+  return d;
+}
+
+// the same descriptor moved `off` bytes forward (off < bytes)
+__device__ __forceinline__ u32x4 buffer_desc_at(u32x4 d, unsigned off) {
+  const unsigned long long b = ((unsigned long long)d[1] << 32 | d[0]) + off;
+  u32x4 r;
+  r[0] = (unsigned)b;
+  r[1] = (unsigned)(b >> 32) & 0xffffu;
+  r[2] = d[2] - off;
+  r[3] = d[3];
+  return r;
 }
 
 // LDS position (16-byte chunk index within the row) of chunk c of row r
@@ -126,16 +144,31 @@ template <int D> __device__ __forceinline__ int vswz(int r, int c) {
 }
 
 // NW direct-to-LDS loads of 1 KiB each: instruction k writes LDS bytes
-// [dst + 1024k, +1024) (16 bytes per lane, in lane order) from the byte offsets
-// goff[k] + base of the buffer.  A plain device function: the builtin exists
-// only for the device, and kernel lambdas are compiled for the host as well.
+// [lds + 1024k, +1024) (16 bytes per lane, in lane order) from the byte offsets
+// goff[k] of the buffer `desc`.  `lds` is a wave-uniform LDS byte address.
+//
+// Issued from inline assembly on purpose: the compiler cannot tell which LDS
+// bytes a direct-to-LDS load writes, so after the builtin form it makes the
+// next LDS read wait for every load in flight, which would serialise each
+// step's prefetch with that step's own reads.  These loads write ring slots
+// that no wave reads before the step_barrier that waits for them (its vmcnt
+// count covers these loads), so no such wait is needed.  M0 holds the LDS
+// destination; it is saved and restored around the loads, and one wait state
+// separates its write from the load that reads it.
 template <int NW>
-__device__ __forceinline__ void dma_block(__amdgpu_buffer_rsrc_t rs, char* dst, const unsigned* goff,
-                                          unsigned base) {
+__device__ __forceinline__ void dma_block(u32x4 desc, unsigned lds, const unsigned* goff) {
 #pragma unroll
-  for (int k = 0; k < NW; ++k)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rs, (__attribute__((address_space(3))) void*)(dst + 1024 * k), 16, goff[k] + base, 0, 0, 0);
+  for (int k = 0; k < NW; ++k) {
+    unsigned saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(lds + 1024u * k), "v"(goff[k]), "s"(desc));
+  }
 }
 
 // end of a step: wait until at most NV vector-memory loads of this wave are in
@@ -157,7 +190,10 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_bf16(FwdArgs a) {
   char* kring = smem;
   char* vring = smem + kKSlots * BLK;
 
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, ln = lane & 31, hf = lane >> 5;
+  // the wave index is the same in every lane: say so, so that everything
+  // derived from it (block ranges, LDS slots, descriptors) stays scalar
+  const int tid = threadIdx.x, lane = tid & 63, ln = lane & 31, hf = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int bid = blockIdx.x;
   const int bh = bid % a.BH;
   const int qb = CAUSAL ? (a.nqb - 1 - bid / a.BH) : bid / a.BH;
@@ -167,8 +203,8 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_bf16(FwdArgs a) {
   const bool qvalid = qrow < N;
   const size_t head = (size_t)bh * N * D;
   const __bf16* Q = (const __bf16*)a.q + head;
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc((const __bf16*)a.k + head, (unsigned)N * RB);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc((const __bf16*)a.v + head, (unsigned)N * RB);
+  const u32x4 kdesc = buffer_desc((const __bf16*)a.k + head, (unsigned)N * RB);
+  const u32x4 vdesc = buffer_desc((const __bf16*)a.v + head, (unsigned)N * RB);
 
   // key blocks: all of them, or (causal) up to the workgroup's last query
   const int nblk = (N + kBc - 1) / kBc;
@@ -199,11 +235,15 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_bf16(FwdArgs a) {
     kgoff[k] = (unsigned)(r * RB + 16 * kswz<D>(r, p));
     vgoff[k] = (unsigned)(r * RB + 16 * vswz<D>(r, p));
   }
+  // wave-uniform LDS byte addresses of this wave's share of ring slot 0
+  const unsigned wu = (unsigned)w;
+  const unsigned lds0 = (unsigned)(unsigned long long)(__attribute__((address_space(3))) char*)smem;
+  const unsigned kdst = lds0 + wu * CHW * 1024, vdst = kdst + kKSlots * BLK;
   auto load_k = [&](int j) {
-    dma_block<CHW>(krs, kring + (j % kKSlots) * BLK + w * CHW * 1024, kgoff, (unsigned)j * BLK);
+    dma_block<CHW>(buffer_desc_at(kdesc, (unsigned)j * BLK), kdst + (j % kKSlots) * BLK, kgoff);
   };
   auto load_v = [&](int j) {
-    dma_block<CHW>(vrs, vring + (j % kVSlots) * BLK + w * CHW * 1024, vgoff, (unsigned)j * BLK);
+    dma_block<CHW>(buffer_desc_at(vdesc, (unsigned)j * BLK), vdst + (j % kVSlots) * BLK, vgoff);
   };
 
   // K operand reads: lane (key ln of tile t, half hf) reads chunk 2kk + hf of
@@ -357,6 +397,9 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_bf16(FwdArgs a) {
   if (jend > 2) load_k(2);
   load_v(0);
   step_barrier<0>();
+  // the same wait in a form the compiler sees: the Q fragments (plain global
+  // loads) are complete from here on, so no wait for them lands in the loop
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0), expcnt and lgkmcnt untouched
   f32x16 s0 = {}, s1 = {};     // S_j, then S_{j+1} (same registers)
   bf16x8 pp[4], pc[4];         // P~_{j-1} and P~_j
 #pragma unroll
