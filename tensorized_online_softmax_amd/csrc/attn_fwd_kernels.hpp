@@ -88,28 +88,33 @@ __device__ __forceinline__ void count_tiles(const FwdArgs& a, const RowState& st
 // the step for key block j it issues, in one instruction stream,
 //   matrix unit : O^T += V_{j-1}^T P~_{j-1}^T   and   S_{j+1} = K_{j+1} Q^T
 //   vector units: the softmax of S_j -> P~_j (tile max, exp2, pack, row sums)
-// with the MFMAs spread evenly between the vector instructions, so that the
-// tensor and vector work of FlashAttention-T (section A2, tensor-vector
-// scheduling) overlap inside the wave, and the second wave on the SIMD fills
-// what one wave leaves idle.  The rescale of O by alpha_j (rare: the surrogate
-// maximum seldom moves) waits until the P~_{j-1} product is in O.
+// with the MFMAs spread between the vector instructions, so that the tensor
+// and vector work of FlashAttention-T (section A2, tensor-vector scheduling)
+// overlap inside the wave, and the second wave on the SIMD fills what one wave
+// leaves idle.  The rescale of O by alpha_j (rare: the surrogate maximum
+// seldom moves) comes after the P~_{j-1} product and before the P~_j one.
 //
-// Key blocks stream into LDS rings (4 slots for K, 3 for V) through buffer
+// Key blocks stream into two LDS rings of 4 slots (K and V) through buffer
 // loads that write LDS directly (no registers; rows past N read as 0).  Step j
-// issues K_{j+3} and V_{j+1}, two steps before their first reads; each
-// overwrites a slot last read two steps earlier.  Every step ends with a plain
-// barrier after waiting until only the loads issued in that step are in
-// flight.  A direct-to-LDS load writes 1 KiB per wave instruction,
-// contiguous, so rows are not padded: 16-byte chunks are XOR-swizzled within
-// each row instead, which keeps the K operand reads (16 rows, one chunk each)
-// and the transposing V reads (4 rows x 2 chunks per 16 lanes) free of LDS bank
-// conflicts.
+// issues K_{j+4} and V_{j+2} into the slots that K_j and V_{j-2} held (read in
+// step j-1); blocks at or past the workgroup's last one are fetched as zeros,
+// so every step issues the same loads.  Every step ends with a plain barrier
+// after waiting until only the loads of the last two steps are in flight.
+// A direct-to-LDS load writes 1 KiB per wave instruction, contiguous, so rows
+// are not padded: 16-byte chunks are XOR-swizzled within each row instead,
+// which keeps the K operand reads (16 rows, one chunk each) and the
+// transposing V reads (4 rows x 2 chunks per 16 lanes) free of bank conflicts.
+//
+// Steady steps run four to a loop iteration (the ring period), so that ring
+// slots are constants folded into the LDS instructions, and S and P~ alternate
+// between two register sets instead of being copied.
 // ---------------------------------------------------------------------------
 constexpr int kPWaves = 8;
 constexpr int kPThreads = 64 * kPWaves;
 constexpr int kPBr = 32 * kPWaves;   // 256 query rows per workgroup
-constexpr int kKSlots = 4;           // LDS ring slots for K
-constexpr int kVSlots = 3;           // LDS ring slots for V
+constexpr int kRing = 4;             // LDS ring slots for K and for V
+constexpr int kKAhead = 4;           // step j loads K_{j+4}
+constexpr int kVAhead = 2;           // step j loads V_{j+2}
 
 // Raw buffer descriptor (stride 0) over [base, base + bytes): loads at offsets
 // at or past `bytes` return zeros.  The fourth word is the gfx9 data format
@@ -124,13 +129,15 @@ __device__ __forceinline__ u32x4 buffer_desc(const void* base, unsigned bytes) {
   return d;
 }
 
-// the same descriptor moved `off` bytes forward (off < bytes)
-__device__ __forceinline__ u32x4 buffer_desc_at(u32x4 d, unsigned off) {
-  const unsigned long long b = ((unsigned long long)d[1] << 32 | d[0]) + off;
+// Descriptor of key block j (blk bytes each) of a head: the buffer moved to
+// the block's start, or, for j >= jlim, an empty one (every load reads zeros).
+__device__ __forceinline__ u32x4 block_desc(u32x4 d, int j, int jlim, unsigned blk) {
+  const unsigned off = (unsigned)j * blk;
+  const unsigned long long b = ((unsigned long long)d[1] << 32 | d[0]) + (j < jlim ? off : 0u);
   u32x4 r;
   r[0] = (unsigned)b;
   r[1] = (unsigned)(b >> 32) & 0xffffu;
-  r[2] = d[2] - off;
+  r[2] = j < jlim ? d[2] - off : 0u;
   r[3] = d[3];
   return r;
 }
@@ -178,17 +185,26 @@ template <int NV> __device__ __forceinline__ void step_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(NV) : "memory");
 }
 
+// keeps x in registers here: the computation of x cannot sink past this point
+template <typename T> __device__ __forceinline__ void pin(const T& x) {
+  asm volatile("" ::"v"(x));
+}
+
+template <int I> struct Int { static constexpr int value = I; };
+
 template <int D, bool CAUSAL, int X, bool ROWSUM_MFMA, bool FB_AUTO>
 __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_bf16(FwdArgs a) {
   static_assert(D == 64 || D == 128, "head dim");
-  constexpr int RB = 2 * D;                 // bytes per K or V row
-  constexpr int BLK = kBc * RB;             // bytes per key block of K or V
+  constexpr int RB = 2 * D;                   // bytes per K or V row
+  constexpr int BLK = kBc * RB;               // bytes per key block of K or V
   constexpr int CHW = BLK / 1024 / kPWaves;   // 1 KiB load instructions per wave per tensor
-  constexpr int NKK = D / 16;  // k-steps of S^T = K Q^T
-  constexpr int NMT = D / 32;  // 32-row M tiles of O^T
-  __shared__ __attribute__((aligned(1024))) char smem[(kKSlots + kVSlots) * BLK];
-  char* kring = smem;
-  char* vring = smem + kKSlots * BLK;
+  constexpr int NKK = D / 16;                 // k-steps of S^T = K Q^T
+  constexpr int NMT = D / 32;                 // 32-row M tiles of O^T
+  constexpr int NV_STEP = 2 * CHW;            // loads a wave issues per step
+  // V ring first: its slot offsets plus the in-block offsets fit the 16-bit
+  // immediate of the LDS reads; the K ring's base is folded into koff
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kRing * BLK];
+  char* vring = smem;
 
   // the wave index is the same in every lane: say so, so that everything
   // derived from it (block ranges, LDS slots, descriptors) stays scalar
@@ -236,21 +252,20 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_bf16(FwdArgs a) {
     vgoff[k] = (unsigned)(r * RB + 16 * vswz<D>(r, p));
   }
   // wave-uniform LDS byte addresses of this wave's share of ring slot 0
-  const unsigned wu = (unsigned)w;
   const unsigned lds0 = (unsigned)(unsigned long long)(__attribute__((address_space(3))) char*)smem;
-  const unsigned kdst = lds0 + wu * CHW * 1024, vdst = kdst + kKSlots * BLK;
+  const unsigned vdst = lds0 + (unsigned)w * CHW * 1024, kdst = vdst + kRing * BLK;
   auto load_k = [&](int j) {
-    dma_block<CHW>(buffer_desc_at(kdesc, (unsigned)j * BLK), kdst + (j % kKSlots) * BLK, kgoff);
+    dma_block<CHW>(block_desc(kdesc, j, jend, BLK), kdst + (j % kRing) * BLK, kgoff);
   };
   auto load_v = [&](int j) {
-    dma_block<CHW>(buffer_desc_at(vdesc, (unsigned)j * BLK), vdst + (j % kVSlots) * BLK, vgoff);
+    dma_block<CHW>(block_desc(vdesc, j, jend, BLK), vdst + (j % kRing) * BLK, vgoff);
   };
 
   // K operand reads: lane (key ln of tile t, half hf) reads chunk 2kk + hf of
   // row 32t + ln; the swizzle depends on the row only through ln
   int koff[NKK];
 #pragma unroll
-  for (int kk = 0; kk < NKK; ++kk) koff[kk] = ln * RB + 16 * kswz<D>(ln, 2 * kk + hf);
+  for (int kk = 0; kk < NKK; ++kk) koff[kk] = kRing * BLK + ln * RB + 16 * kswz<D>(ln, 2 * kk + hf);
   // V transposing reads: lane (16-lane group G, index i) reads 8 bytes of row
   // 16s + 4(G/2) + i/4 (+8 for slots 4..7) at element 32mt + 16(G%2) + 4(i%4),
   // i.e. chunk 4mt + 2(G%2) + (i%4)/2, byte 8((i%4)%2) within it
@@ -275,9 +290,10 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_bf16(FwdArgs a) {
   for (int t = 0; t < 8; ++t) ones[t] = (__bf16)1.0f;
   const bf16x2 ones2 = {(__bf16)1.0f, (__bf16)1.0f};
 
-  // S^T = K_j Q^T into (t0, t1), two 32-key tiles
-  auto qk = [&](int j, f32x16& t0, f32x16& t1) {
-    const char* kt = kring + (j % kKSlots) * BLK;
+  // S^T = K_j Q^T into (t0, t1), two 32-key tiles, for the K block in ring
+  // slot `slot` (koff holds the K ring's offset in smem)
+  auto qk = [&](int slot, f32x16& t0, f32x16& t1) {
+    const char* kt = smem + slot * BLK;
     t0 = f32x16{};
     t1 = f32x16{};
 #pragma unroll
@@ -288,11 +304,11 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_bf16(FwdArgs a) {
       t1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[kk], t1, 0, 0, 0);
     }
   };
-  // O^T += V_j^T P~^T, 16 keys per step.  Step s, slot t of lane half h is
-  // key 16s + 8(t/4) + 4h + t%4 (the accumulator order of S^T), which the
-  // transposing reads above fetch.
-  auto pv = [&](int j, const bf16x8* pk) {
-    const char* vt = vring + (j % kVSlots) * BLK;
+  // O^T += V^T P~^T for the V block in ring slot `slot`, 16 keys per step.
+  // Step s, slot t of lane half h is key 16s + 8(t/4) + 4h + t%4 (the
+  // accumulator order of S^T), which the transposing reads above fetch.
+  auto pv = [&](int slot, const bf16x8* pk) {
+    const char* vt = vring + slot * BLK;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
 #pragma unroll
@@ -326,12 +342,17 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_bf16(FwdArgs a) {
       }
     }
     // step 1 and the reference update (steps 2-3); rows past N stay out of the
-    // tile maximum
-    float bm = fmax_raw(s0[0], s0[1]);
+    // tile maximum.  Four independent max chains.
+    float bm4[4];
 #pragma unroll
-    for (int r = 2; r < 16; ++r) bm = fmax_raw(bm, s0[r]);
+    for (int q = 0; q < 4; ++q) bm4[q] = fmax_raw(s0[4 * q], s0[4 * q + 1]);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) bm = fmax_raw(bm, s1[r]);
+    for (int q = 0; q < 4; ++q) {
+      bm4[q] = fmax_raw(bm4[q], fmax_raw(s0[4 * q + 2], s0[4 * q + 3]));
+#pragma unroll
+      for (int r = 0; r < 4; ++r) bm4[q] = fmax_raw(bm4[q], s1[4 * q + r]);
+    }
+    float bm = fmax_raw(fmax_raw(bm4[0], bm4[1]), fmax_raw(bm4[2], bm4[3]));
     bm = qvalid ? bm : -__builtin_inff();
     const float alpha = row_state_update<X, FB_AUTO>(st, bm, c, tau);
     // steps 4-6: P~ = exp2(c*S - c*ref), packed to bf16 as the B operand
@@ -374,72 +395,76 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_bf16(FwdArgs a) {
       if constexpr (ROWSUM_MFMA) lacc *= alpha;
     }
   };
-
-  // Loads issued in step j (K_{j+3}, V_{j+1}) and the end-of-step barrier:
-  // only the loads issued in this step may still be in flight after it.
   auto step_loads = [&](int j) {
-    if (j + 3 < jend) load_k(j + 3);
-    if (j + 1 < jend) load_v(j + 1);
-  };
-  auto step_end = [&](int j) {
-    const int nk = (j + 3 < jend) ? CHW : 0, nv = (j + 1 < jend) ? CHW : 0;
-    if (nk + nv == 2 * CHW)
-      step_barrier<2 * CHW>();
-    else if (nk + nv == CHW)
-      step_barrier<CHW>();
-    else
-      step_barrier<0>();
+    load_k(j + kKAhead);
+    load_v(j + kVAhead);
   };
 
-  // ---- prologue: K_0, K_1, K_2 and V_0 into the rings, then S_0
-  load_k(0);
-  if (jend > 1) load_k(1);
-  if (jend > 2) load_k(2);
-  load_v(0);
+  // ---- prologue: K_0..K_3 and V_0, V_1 into the rings, then S_0
+#pragma unroll
+  for (int j = 0; j < kKAhead; ++j) load_k(j);
+#pragma unroll
+  for (int j = 0; j < kVAhead; ++j) load_v(j);
   step_barrier<0>();
   // the same wait in a form the compiler sees: the Q fragments (plain global
   // loads) are complete from here on, so no wait for them lands in the loop
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0), expcnt and lgkmcnt untouched
-  f32x16 s0 = {}, s1 = {};     // S_j, then S_{j+1} (same registers)
-  bf16x8 pp[4], pc[4];         // P~_{j-1} and P~_j
-#pragma unroll
-  for (int t = 0; t < 4; ++t) pp[t] = pc[t] = bf16x8{};
-  if (jend_w > 0) qk(0, s0, s1);
 
-  // Three phases, so that the steady loop has a single path and its loop
-  // carried registers (S, P~, O) are updated in place:
-  //   first step (j = 0), steady steps (1 <= j < jend_w - 1), then the wave's
-  //   last block, the final P~V product and the idle steps up to jend.
-  // Each step (any phase) issues its loads and ends with the barrier, so every
-  // wave passes the same jend + 1 barriers.
+  // Register sets: entering any step j, S_j is in S[0] and P~_{j-1} in P[1].
+  f32x16 S[2][2];
+  bf16x8 P[2][4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) P[0][t] = P[1][t] = bf16x8{};
+  S[0][0] = S[0][1] = S[1][0] = S[1][1] = f32x16{};
+  if (jend_w > 0) qk(0, S[0][0], S[0][1]);
+  // step 0 refills K_0's slot: every wave must be done reading it
+  step_barrier<0>();
+
+  // Any step (first, last, idle), slots and masking decided at run time.
   auto edge_step = [&](int j) {
     step_loads(j);
-    if (j >= 1 && j <= jend_w) pv(j - 1, pp);
+    if (j >= 1 && j <= jend_w) pv((j - 1) % kRing, P[1]);
     if (j < jend_w) {
-      const float alpha = softmax(j, s0, s1, pc, j == jend_w - 1);
-      if (j + 1 < jend_w) qk(j + 1, s0, s1);
+      const float alpha = softmax(j, S[0][0], S[0][1], P[0], j == jend_w - 1);
+      if (j + 1 < jend_w) qk((j + 1) % kRing, S[0][0], S[0][1]);
       rescale(alpha);
     }
-    step_end(j);
+    step_barrier<2 * NV_STEP>();
 #pragma unroll
-    for (int t = 0; t < 4; ++t) pp[t] = pc[t];
+    for (int t = 0; t < 4; ++t) P[1][t] = P[0][t];
   };
-  int j = 0;
-  if (jend >= 0) edge_step(j++);
-  for (; j + 1 < jend_w; ++j) {
-    // steady state, one instruction stream: P~_{j-1} V_{j-1} and the softmax
-    // of S_j, then S_{j+1} into the same registers
+  // Steady step j = 1 + 4g + u (u = 0..3): a full block that is not the
+  // wave's last.  P~_{j-1} V_{j-1}, the softmax of S_j and S_{j+1} = K_{j+1} Q^T
+  // form one straight-line block; S and P~ alternate between the two sets.
+  auto steady_step = [&](auto U, int j) {
+    constexpr int u = decltype(U)::value;
+    constexpr int cur = u & 1, nxt = cur ^ 1;
     step_loads(j);
-    pv(j - 1, pp);
-    const float alpha = softmax(j, s0, s1, pc, false);
-    __builtin_amdgcn_sched_barrier(0);
-    qk(j + 1, s0, s1);
+    pv(u % kRing, P[nxt]);                                       // V_{j-1}
+    const float alpha = softmax(j, S[cur][0], S[cur][1], P[cur], false);
+    qk((u + 2) % kRing, S[nxt][0], S[nxt][1]);                   // K_{j+1}
+    pin(P[cur][0]);
+    pin(P[cur][1]);
+    pin(P[cur][2]);
+    pin(P[cur][3]);
+    pin(lexact);
+    if constexpr (!ROWSUM_MFMA) pin(lsum);
+    step_barrier<2 * NV_STEP>();
     rescale(alpha);
-    step_end(j);
-#pragma unroll
-    for (int t = 0; t < 4; ++t) pp[t] = pc[t];
+  };
+
+  int j = 0;
+  edge_step(j++);
+  for (; j + 4 < jend_w; j += 4) {
+    steady_step(Int<0>(), j);
+    steady_step(Int<1>(), j + 1);
+    steady_step(Int<2>(), j + 2);
+    steady_step(Int<3>(), j + 3);
   }
   for (; j <= jend; ++j) edge_step(j);
+  // the last steps' loads (zeros past the last block) still write LDS: let
+  // them land before the workgroup can end and its LDS be handed on
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // ---- epilogue: l, O / l, lse (reading R-7: lse = scale*ref + ln l)
   float l;
