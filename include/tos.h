@@ -95,7 +95,9 @@ typedef struct {
 /*
  * tos_attn_fwd -- O = softmax(scale * Q K^T) V and lse, as described above.
  *
- *   q, k, v   device pointers, [B][H][N][d] of `dtype` (see tos_dtype)
+ *   q, k, v   device pointers, [B][H][N][d] of `dtype` (see tos_dtype); the
+ *             values must be finite (NaN or infinite inputs give unspecified
+ *             outputs)
  *   o         device pointer, [B][H][N][d]: float32 for TOS_F32, bfloat16
  *             otherwise; must not overlap q, k, v or lse
  *   lse       device pointer to [B][H][N] float32 natural-log log-sum-exp of the

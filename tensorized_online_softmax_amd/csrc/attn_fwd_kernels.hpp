@@ -185,12 +185,19 @@ template <int NV> __device__ __forceinline__ void step_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(NV) : "memory");
 }
 
-// keeps x in registers here: the computation of x cannot sink past this point
+// keeps x in registers here: the computation of x cannot sink past this point.
+// (Device pass only: kernel lambdas are also parsed for the host, where a
+// vector-register operand of this width does not exist.)
 template <typename T> __device__ __forceinline__ void pin(const T& x) {
+#if defined(__HIP_DEVICE_COMPILE__)
   asm volatile("" ::"v"(x));
+#else
+  (void)x;
+#endif
 }
 
 template <int I> struct Int { static constexpr int value = I; };
+
 
 template <int D, bool CAUSAL, int X, bool ROWSUM_MFMA, bool FB_AUTO>
 __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_bf16(FwdArgs a) {
@@ -290,101 +297,109 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_bf16(FwdArgs a) {
   for (int t = 0; t < 8; ++t) ones[t] = (__bf16)1.0f;
   const bf16x2 ones2 = {(__bf16)1.0f, (__bf16)1.0f};
 
-  // S^T = K_j Q^T into (t0, t1), two 32-key tiles, for the K block in ring
-  // slot `slot` (koff holds the K ring's offset in smem)
+  // ---- operands and single matrix instructions
+  // QK instruction g (0 <= g < NQK) of S^T = K Q^T: key tile t = g % 2,
+  // k-step kk = g / 2; its K operand comes from the K block at kt
+  constexpr int NQK = 2 * NKK, NPV = 4 * NMT;
+  auto kread = [&](const char* kt, int g) -> bf16x8 {
+    return *(const bf16x8*)(kt + koff[g / 2] + (g % 2) * 32 * RB);
+  };
+  auto qk_mfma = [&](int g, bf16x8 av, f32x16& t0, f32x16& t1) {
+    f32x16& acc = (g % 2) ? t1 : t0;
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[g / 2], g < 2 ? f32x16{} : acc, 0, 0, 0);
+  };
+  // PV instruction i (0 <= i < NPV) of O^T += V^T P~^T: 16-key step s = i / NMT,
+  // M tile mt = i % NMT.  Step s, slot t of lane half h is key
+  // 16s + 8(t/4) + 4h + t%4 (the accumulator order of S^T), which the
+  // transposing reads fetch.
+  auto vread = [&](const char* vt, int i) -> bf16x8 {
+    const char* p = vt + voff[i % NMT] + 16 * (i / NMT) * RB;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p + 8 * RB));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  auto pv_mfma = [&](int i, bf16x8 av, const bf16x8* pk) {
+    oacc[i % NMT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pk[i / NMT], oacc[i % NMT], 0, 0, 0);
+    if constexpr (ROWSUM_MFMA)   // step 7 on the matrix unit: ones x P~^T
+      if (i % NMT == NMT - 1)
+        lacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pk[i / NMT], lacc, 0, 0, 0);
+  };
   auto qk = [&](int slot, f32x16& t0, f32x16& t1) {
     const char* kt = smem + slot * BLK;
-    t0 = f32x16{};
-    t1 = f32x16{};
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      const bf16x8 a0 = *(const bf16x8*)(kt + koff[kk]);
-      const bf16x8 a1 = *(const bf16x8*)(kt + koff[kk] + 32 * RB);
-      t0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[kk], t0, 0, 0, 0);
-      t1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[kk], t1, 0, 0, 0);
-    }
+    for (int g = 0; g < NQK; ++g) qk_mfma(g, kread(kt, g), t0, t1);
   };
-  // O^T += V^T P~^T for the V block in ring slot `slot`, 16 keys per step.
-  // Step s, slot t of lane half h is key 16s + 8(t/4) + 4h + t%4 (the
-  // accumulator order of S^T), which the transposing reads above fetch.
   auto pv = [&](int slot, const bf16x8* pk) {
     const char* vt = vring + slot * BLK;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-#pragma unroll
-      for (int mt = 0; mt < NMT; ++mt) {
-        const char* p = vt + voff[mt] + 16 * s * RB;
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4*)(p));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4*)(p + 8 * RB));
-        const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        oacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pk[s], oacc[mt], 0, 0, 0);
-      }
-      if constexpr (ROWSUM_MFMA)   // step 7 on the matrix unit: ones x P~^T
-        lacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pk[s], lacc, 0, 0, 0);
-    }
+    for (int i = 0; i < NPV; ++i) pv_mfma(i, vread(vt, i), pk);
   };
-  // Steps 1-7 of Algorithm 1 for key block j: logits (s0, s1) -> P~ in pk.
-  // The vector row sums absorb alpha at once; the returned alpha still has to
-  // be applied to the matrix accumulators (O, and l on the MFMA) once the
-  // previous block's P~V product has landed in them.
-  auto softmax = [&](int j, f32x16& s0, f32x16& s1, bf16x8* pk, bool masked) -> float {
-    if (masked) {
-      // only a wave's last block can hold keys past the diagonal or past N:
-      // key of register r of tile t is kb + 32t + 8(r/4) + 4hf + r%4
-      const int kb = j * kBc;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = kb + 8 * (r / 4) + 4 * hf + (r % 4);
-        if (key >= klim) s0[r] = -__builtin_inff();
-        if (key + 32 >= klim) s1[r] = -__builtin_inff();
-      }
-    }
-    // step 1 and the reference update (steps 2-3); rows past N stay out of the
-    // tile maximum.  Four independent max chains.
-    float bm4[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) bm4[q] = fmax_raw(s0[4 * q], s0[4 * q + 1]);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      bm4[q] = fmax_raw(bm4[q], fmax_raw(s0[4 * q + 2], s0[4 * q + 3]));
-#pragma unroll
-      for (int r = 0; r < 4; ++r) bm4[q] = fmax_raw(bm4[q], s1[4 * q + r]);
-    }
-    float bm = fmax_raw(fmax_raw(bm4[0], bm4[1]), fmax_raw(bm4[2], bm4[3]));
-    bm = qvalid ? bm : -__builtin_inff();
-    const float alpha = row_state_update<X, FB_AUTO>(st, bm, c, tau);
-    // steps 4-6: P~ = exp2(c*S - c*ref), packed to bf16 as the B operand
-    const float nb = neg_c_ref(st, c);
-    float pe0 = 0.0f, pe1 = 0.0f;
+
+  // ---- the softmax of one key block, in pieces (Algorithm 1)
+  // Key of register r of tile t in block j: j*Bc + 32t + 8(r/4) + 4hf + r%4.
+  // Only a wave's last block can hold keys past the diagonal or past N.
+  auto mask_block = [&](int j, f32x16& s0, f32x16& s1) {
+    const int kb = j * kBc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], c, nb));
-      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], c, nb));
-      pe0 += p0;
-      pe1 += p1;
-      pk[r / 8][r % 8] = (__bf16)p0;
-      pk[2 + r / 8][r % 8] = (__bf16)p1;
+      const int key = kb + 8 * (r / 4) + 4 * hf + (r % 4);
+      if (key >= klim) s0[r] = -__builtin_inff();
+      if (key + 32 >= klim) s1[r] = -__builtin_inff();
     }
-    // two row sums (step 7): the unrounded one gives lse; the one over the
-    // rounded P~ the P~V product consumes normalises O, so O / l stays a
-    // weighted average of V rows (bf16 rounding of P~ then cancels to first
-    // order instead of adding to the error of O)
-    lexact = lexact * alpha + (pe0 + pe1);
-    if constexpr (!ROWSUM_MFMA) {
-      // on the vector unit: dot products of each packed pair with (1, 1)
-      float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  };
+  // step 1, in four chains of 8 logits: part q covers registers 8q'..8q'+7
+  // of tile q/2 (q' = q % 2)
+  float bm4[4];
+  auto max_part = [&](int q, const f32x16& s0, const f32x16& s1) {
+    const f32x16& sv = (q / 2) ? s1 : s0;
+    const int r0 = 8 * (q % 2);
+    float m = fmax_raw(sv[r0], sv[r0 + 1]);
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        ps[0] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pk[s], pk[s], 0, 1), ones2, ps[0], false);
-        ps[1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pk[s], pk[s], 2, 3), ones2, ps[1], false);
-        ps[2] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pk[s], pk[s], 4, 5), ones2, ps[2], false);
-        ps[3] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pk[s], pk[s], 6, 7), ones2, ps[3], false);
-      }
-      lsum = lsum * alpha + ((ps[0] + ps[1]) + (ps[2] + ps[3]));
-    }
-    return alpha;
+    for (int r = r0 + 2; r < r0 + 8; r += 2) m = fmax_raw(m, fmax_raw(sv[r], sv[r + 1]));
+    bm4[q] = m;
+  };
+  // steps 2-3: running row maxima and the lane-pair combine; rows past N stay
+  // out of the tile maximum
+  auto max_combine = [&]() {
+    float bm = fmax_raw(fmax_raw(bm4[0], bm4[1]), fmax_raw(bm4[2], bm4[3]));
+    bm = qvalid ? bm : -__builtin_inff();
+    row_max_update(st, bm);
+  };
+  // the tile maximum (the surrogate) and the new reference: alpha, and
+  // -c * ref for the exponentials
+  float ref_new = 0.0f;
+  auto tile_ref = [&]() { ref_new = block_ref<X, FB_AUTO>(st, c, tau); };
+  auto advance = [&](float& alpha, float& nb) {
+    alpha = ref_advance(st, ref_new, c);
+    nb = neg_c_ref(st, c);
+  };
+  // steps 4-7 for registers r, r+1 of tile t (unit k: t = k / 8,
+  // r = 2 (k % 8)): P~ = exp2(c*S - c*ref), packed to bf16 as the B operand
+  // of the P~V product, and both row sums.  The unrounded sum gives lse; the
+  // sum of the rounded P~ that the product consumes normalises O, so O / l
+  // stays a weighted average of V rows (bf16 rounding of P~ then cancels to
+  // first order instead of adding to the error of O).
+  float pe[2], ps[2];
+  auto sums_reset = [&]() { pe[0] = pe[1] = ps[0] = ps[1] = 0.0f; };
+  auto exp_unit = [&](int k, const f32x16& s0, const f32x16& s1, bf16x8* pk, float nb) {
+    const int t = k / 8, r = 2 * (k % 8);
+    const f32x16& sv = t ? s1 : s0;
+    const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r], c, nb));
+    const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r + 1], c, nb));
+    pe[t] += p0;
+    pe[t] += p1;
+    bf16x2 w;
+    w[0] = (__bf16)p0;
+    w[1] = (__bf16)p1;
+    pk[2 * t + r / 8][r % 8] = w[0];
+    pk[2 * t + r / 8][r % 8 + 1] = w[1];
+    if constexpr (!ROWSUM_MFMA) ps[t] = __builtin_amdgcn_fdot2_f32_bf16(w, ones2, ps[t], false);
+  };
+  // the block's sums into the running ones (which absorb alpha here; O and the
+  // MFMA row sum get alpha at the end of the step)
+  auto sums_commit = [&](float alpha) {
+    lexact = lexact * alpha + (pe[0] + pe[1]);
+    if constexpr (!ROWSUM_MFMA) lsum = lsum * alpha + (ps[0] + ps[1]);
   };
   // alpha on the matrix accumulators; the whole wave skips it when no row's
   // reference moved (alpha == 1 everywhere, the common case)
@@ -400,7 +415,7 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_bf16(FwdArgs a) {
     load_v(j + kVAhead);
   };
 
-  // ---- prologue: K_0..K_3 and V_0, V_1 into the rings, then S_0
+  // ---- prologue: K_0..K_3 and V_0, V_1 into the rings
 #pragma unroll
   for (int j = 0; j < kKAhead; ++j) load_k(j);
 #pragma unroll
@@ -410,39 +425,124 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_bf16(FwdArgs a) {
   // loads) are complete from here on, so no wait for them lands in the loop
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0), expcnt and lgkmcnt untouched
 
-  // Register sets: entering any step j, S_j is in S[0] and P~_{j-1} in P[1].
+  // Pipeline of key block b: S_b = K_b Q^T and its tile maximum in step b-1,
+  // its exponentials and row sums in step b, P~_b V_b in step b+1; O is
+  // rescaled by alpha_b at the end of step b (after P~_{b-1} V_{b-1}, before
+  // P~_b V_b).  Entering step j: S_j (masked if it is the wave's last block)
+  // in S[0], P~_{j-1} in P[1], alpha_j and -c ref_j in alpha_cur, nb_cur.
   f32x16 S[2][2];
   bf16x8 P[2][4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) P[0][t] = P[1][t] = bf16x8{};
   S[0][0] = S[0][1] = S[1][0] = S[1][1] = f32x16{};
-  if (jend_w > 0) qk(0, S[0][0], S[0][1]);
+  float alpha_cur = 1.0f, nb_cur = 0.0f, alpha_nxt = 1.0f, nb_nxt = 0.0f;
+  // whole-block softmax state (tile maximum and reference) of S_j in (s0, s1)
+  auto block_state = [&](int j, f32x16& s0, f32x16& s1, float& alpha, float& nb) {
+    if (j == jend_w - 1) mask_block(j, s0, s1);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) max_part(q, s0, s1);
+    max_combine();
+    tile_ref();
+    advance(alpha, nb);
+  };
+  if (jend_w > 0) {
+    qk(0, S[0][0], S[0][1]);
+    block_state(0, S[0][0], S[0][1], alpha_cur, nb_cur);
+  }
   // step 0 refills K_0's slot: every wave must be done reading it
   step_barrier<0>();
 
   // Any step (first, last, idle), slots and masking decided at run time.
   auto edge_step = [&](int j) {
     step_loads(j);
-    if (j >= 1 && j <= jend_w) pv((j - 1) % kRing, P[1]);
     if (j < jend_w) {
-      const float alpha = softmax(j, S[0][0], S[0][1], P[0], j == jend_w - 1);
-      if (j + 1 < jend_w) qk((j + 1) % kRing, S[0][0], S[0][1]);
-      rescale(alpha);
+      sums_reset();
+#pragma unroll
+      for (int k = 0; k < 16; ++k) exp_unit(k, S[0][0], S[0][1], P[0], nb_cur);
+      sums_commit(alpha_cur);
     }
+    if (j + 1 < jend_w) qk((j + 1) % kRing, S[0][0], S[0][1]);
+    if (j >= 1 && j <= jend_w) pv((j - 1) % kRing, P[1]);
+    if (j + 1 < jend_w) block_state(j + 1, S[0][0], S[0][1], alpha_nxt, nb_nxt);
     step_barrier<2 * NV_STEP>();
+    if (j < jend_w) rescale(alpha_cur);
+    alpha_cur = alpha_nxt;
+    nb_cur = nb_nxt;
 #pragma unroll
     for (int t = 0; t < 4; ++t) P[1][t] = P[0][t];
   };
-  // Steady step j = 1 + 4g + u (u = 0..3): a full block that is not the
-  // wave's last.  P~_{j-1} V_{j-1}, the softmax of S_j and S_{j+1} = K_{j+1} Q^T
-  // form one straight-line block; S and P~ alternate between the two sets.
+
+  // Steady step j = 1 + 4g + u (u = 0..3): j >= 1 and S_{j+1} is not the
+  // wave's last block.  Two phases of one straight-line block, each a run of
+  // chunks of one matrix instruction and a share of the vector work:
+  //   A: S_{j+1} = K_{j+1} Q^T          with the exponentials of S_j (part)
+  //   B: O^T += V_{j-1}^T P~_{j-1}^T    with the tile maximum of S_{j+1} and
+  //                                     the rest of the exponentials of S_j
+  // Operand reads run three instructions ahead.  S and P~ alternate between
+  // the two register sets.
+  // Vector work per chunk, spread evenly (two waves share a SIMD and run the
+  // same chunk at about the same time, so the even spread suits both):
+  //   phase A: exponential units 0..EA-1, unit k in chunk k*NQK/EA
+  //   phase B: the tile-maximum chain of S_{j+1} in its first chunks (d=128:
+  //            parts 0-1 | 2-3 | combine | tile max | advance; d=64: parts
+  //            0-3 | combine, tile max | advance), then units EA..15 spread
+  //            over the chunks after it
+  constexpr int EA = NQK >= 16 ? 10 : 8;       // exponential units in phase A
+  constexpr int MAXC = NPV >= 16 ? 5 : 3;      // phase-B chunks of the maximum chain
+  constexpr int LA = 3;                        // operand read lookahead
+  auto max_chunk = [&](int i, f32x16& n0, f32x16& n1) {
+    if constexpr (NPV >= 16) {
+      if (i == 0) { max_part(0, n0, n1); max_part(1, n0, n1); }
+      if (i == 1) { max_part(2, n0, n1); max_part(3, n0, n1); }
+      if (i == 2) max_combine();
+      if (i == 3) tile_ref();
+      if (i == 4) advance(alpha_nxt, nb_nxt);
+    } else {
+      if (i == 0) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) max_part(q, n0, n1);
+      }
+      if (i == 1) { max_combine(); tile_ref(); }
+      if (i == 2) advance(alpha_nxt, nb_nxt);
+    }
+  };
   auto steady_step = [&](auto U, int j) {
     constexpr int u = decltype(U)::value;
     constexpr int cur = u & 1, nxt = cur ^ 1;
+    const char* kt = smem + ((u + 2) % kRing) * BLK;    // K_{j+1}
+    const char* vt = vring + (u % kRing) * BLK;         // V_{j-1}
+    f32x16 &c0 = S[cur][0], &c1 = S[cur][1], &n0 = S[nxt][0], &n1 = S[nxt][1];
     step_loads(j);
-    pv(u % kRing, P[nxt]);                                       // V_{j-1}
-    const float alpha = softmax(j, S[cur][0], S[cur][1], P[cur], false);
-    qk((u + 2) % kRing, S[nxt][0], S[nxt][1]);                   // K_{j+1}
+    bf16x8 kop[LA], vop[LA];
+#pragma unroll
+    for (int g = 0; g < LA; ++g) kop[g] = kread(kt, g);
+    sums_reset();
+    // phase A
+#pragma unroll
+    for (int g = 0; g < NQK; ++g) {
+      const bf16x8 av = kop[g % LA];
+      if (g + LA < NQK) kop[g % LA] = kread(kt, g + LA);
+      else vop[(g + LA - NQK) % LA] = vread(vt, g + LA - NQK);
+      qk_mfma(g, av, n0, n1);
+#pragma unroll
+      for (int k = 0; k < EA; ++k)
+        if (k * NQK / EA == g) exp_unit(k, c0, c1, P[cur], nb_cur);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // phase B
+#pragma unroll
+    for (int i = 0; i < NPV; ++i) {
+      const bf16x8 av = vop[i % LA];
+      if (i + LA < NPV) vop[i % LA] = vread(vt, i + LA);
+      pv_mfma(i, av, P[nxt]);
+      max_chunk(i, n0, n1);
+#pragma unroll
+      for (int k = EA; k < 16; ++k)
+        if (MAXC - 1 + (k - EA + 1) * (NPV - MAXC + 1) / (16 - EA + 1) == i)
+          exp_unit(k, c0, c1, P[cur], nb_cur);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    sums_commit(alpha_cur);
     pin(P[cur][0]);
     pin(P[cur][1]);
     pin(P[cur][2]);
@@ -450,12 +550,14 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_bf16(FwdArgs a) {
     pin(lexact);
     if constexpr (!ROWSUM_MFMA) pin(lsum);
     step_barrier<2 * NV_STEP>();
-    rescale(alpha);
+    rescale(alpha_cur);
+    alpha_cur = alpha_nxt;
+    nb_cur = nb_nxt;
   };
 
   int j = 0;
   edge_step(j++);
-  for (; j + 4 < jend_w; j += 4) {
+  for (; j + 5 < jend_w; j += 4) {
     steady_step(Int<0>(), j);
     steady_step(Int<1>(), j + 1);
     steady_step(Int<2>(), j + 2);

@@ -74,38 +74,52 @@ __device__ __forceinline__ void row_state_init(RowState& st, bool per_row) {
   st.per_row = per_row;
 }
 
-// Algorithm 1 step 1 (tile max) and the reference update for one key block.
+// Algorithm 1 step 1 (tile max) and the reference update for one key block,
+// in three parts so that callers can spread them between matrix instructions.
 // `blk_max` is this lane's maximum over its logits of the block (before the
-// pair combine).  Returns alpha = exp2(c*(ref_old - ref_new)) (0 when nothing
-// was accumulated yet, 1 when the row still has no key) and updates the state.
-template <int X, bool FB_AUTO>
-__device__ __forceinline__ float row_state_update(RowState& st, float blk_max, float c, float tau) {
-  // straight-line code (selects, no branches), so that the caller's matrix
-  // instructions can be interleaved with it in one basic block
-  const float ninf = -__builtin_inff();
+// pair combine).
+__device__ __forceinline__ void row_max_update(RowState& st, float blk_max) {
   st.m_run = fmax_raw(st.m_run, pair_reduce(blk_max, MaxOp()));
-  float ref_new;
+}
+
+// The block's reference: the tile maximum of the running row maxima (the
+// surrogate), or the row's own maximum once its tile went per-row.
+// Straight-line code (selects, no branches), so that the caller's matrix
+// instructions can be interleaved with it in one basic block.
+template <int X, bool FB_AUTO>
+__device__ __forceinline__ float block_ref(RowState& st, float c, float tau) {
   if constexpr (X == 1) {
-    ref_new = st.m_run;
+    return st.m_run;
   } else {
     const float tm = tile_reduce<X>(st.m_run, MaxOp());
     if constexpr (FB_AUTO) {
       // rows without a key yet cannot underflow: leave them out of the min
+      const float ninf = -__builtin_inff();
       const float mn = tile_reduce<X>(st.m_run == ninf ? __builtin_inff() : st.m_run, MinOp());
       st.per_row = st.per_row || (c * (tm - mn) > tau);
-      ref_new = st.per_row ? st.m_run : tm;
+      return st.per_row ? st.m_run : tm;
     } else {
-      ref_new = tm;
+      return tm;
     }
   }
-  // alpha = exp2(c*(ref_old - ref_new)); 0 when nothing was accumulated yet,
-  // 1 when the row still has no key
+}
+
+// Moves the reference to ref_new.  Returns alpha = exp2(c*(ref_old - ref_new)):
+// 0 when nothing was accumulated yet, 1 when the row still has no key.
+__device__ __forceinline__ float ref_advance(RowState& st, float ref_new, float c) {
+  const float ninf = -__builtin_inff();
   const bool none_yet = st.ref == ninf, no_key = ref_new == ninf;
   const float arg = (none_yet || no_key) ? 0.0f : c * (st.ref - ref_new);
   float alpha = __builtin_amdgcn_exp2f(arg);
   alpha = none_yet ? 0.0f : alpha;
   st.ref = ref_new;
   return alpha;
+}
+
+template <int X, bool FB_AUTO>
+__device__ __forceinline__ float row_state_update(RowState& st, float blk_max, float c, float tau) {
+  row_max_update(st, blk_max);
+  return ref_advance(st, block_ref<X, FB_AUTO>(st, c, tau), c);
 }
 
 // -c * ref, with a row that has no key yet mapped to 0 (its logits are all -inf,
