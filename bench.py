@@ -26,6 +26,7 @@ sys.path.insert(0, ROOT)
 PEAK_TFLOPS = {"bf16": 2516.6, "fp8": 5033.2, "f32": 157.3}   # MI355X dense MFMA
 HBM_GBPS = 8000.0
 KERNEL_SOURCES = ["tensorized_online_softmax_amd/csrc/attn_fwd_kernels.hpp",
+                  "tensorized_online_softmax_amd/csrc/attn_fwd_fp8.hpp",
                   "tensorized_online_softmax_amd/csrc/softmax_tile.hpp"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_{workload}.txt")
 
@@ -95,7 +96,8 @@ def main():
     ap.add_argument("--workload", default="causal_bf16")
     ap.add_argument("--split", default="valu", choices=["valu", "rowsum_mfma"])
     ap.add_argument("--x-tile", type=int, default=None)
-    ap.add_argument("--fallback", default="off", choices=["off", "auto", "force"])
+    ap.add_argument("--fallback", default=None, choices=["off", "auto", "force"],
+                    help="default: the workload's own (AUTO for the fp8 stress workload)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=0, help="0 = every row")
     ap.add_argument("--copy-calib-mib", type=int, default=0)
@@ -111,8 +113,10 @@ def main():
 
     w = inputs.WORKLOADS[args.workload]
     x_tile = args.x_tile or w.x_tile
+    fallback = args.fallback or w.fallback
     print(f"[bench] workload {w.name}: B={w.B} H={w.H} N={w.N} d={w.d} {w.dtype} "
-          f"causal={w.causal} X={x_tile} split={args.split}", file=sys.stderr, flush=True)
+          f"causal={w.causal} X={x_tile} split={args.split} fallback={fallback}",
+          file=sys.stderr, flush=True)
     inp = inputs.make_workload(w)
     torch.cuda.set_device(0)
     q, k, v = (inp[n].cuda() for n in ("q", "k", "v"))
@@ -123,7 +127,7 @@ def main():
 
     def step():
         binding.attn_fwd(q, k, v, causal=w.causal, scale=w.scale, dtype=w.dtype,
-                         x_tile=x_tile, split=args.split, fallback=args.fallback,
+                         x_tile=x_tile, split=args.split, fallback=fallback,
                          descale=descale, out=o, lse=lse)
 
     for _ in range(args.warmup):
@@ -176,8 +180,10 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic (seeded N(0,1) inputs, numpy PCG64)",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
-                   "causal": w.causal, "x_tile": x_tile, "softmax_split": args.split,
-                   "fallback": args.fallback, "Br": 128 if w.dtype == "f32" else 256, "Bc": 64,
+                   "causal": w.causal, "x_tile": x_tile,
+                   # e4m3 P~ pairs have no vector dot form: fp8 sums them on the matrix unit
+                   "softmax_split": "rowsum_mfma" if w.dtype == "fp8" else args.split,
+                   "fallback": fallback, "Br": 128 if w.dtype == "f32" else 256, "Bc": 64,
                    "flops_per_step": flops, "pct_of_peak": round(100 * achieved / peak, 2)},
         "roofline": roofline,
     }

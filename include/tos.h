@@ -54,16 +54,21 @@ typedef enum {
     TOS_F32 = 0,       /* q, k, v, o: float32                                       */
     TOS_BF16 = 1,      /* q, k, v, o: bfloat16                                      */
     TOS_FP8_E4M3 = 2   /* q, k, v: OCP float8 e4m3fn codes (x = descale * code);
-                          o: bfloat16; descales are required in the options       */
+                          o: bfloat16; descales are required in the options;
+                          d = 128 only (other head dims: TOS_ERR_UNSUPPORTED)     */
 } tos_dtype;
 
 /* How the softmax row sum l is computed (FlashAttention-T section A2,
  * "row-sum reduction", Fig 5(b)). */
 typedef enum {
-    TOS_SPLIT_VALU = 0,         /* vector-unit adds of P~ in fp32                   */
+    TOS_SPLIT_VALU = 0,         /* vector-unit dot products of the packed P~ pairs
+                                   with (1, 1)                                      */
     TOS_SPLIT_ROWSUM_MFMA = 1   /* matrix-unit contraction of the packed P~ against a
-                                   constant all-ones operand (bf16 only)            */
+                                   constant all-ones operand (bf16; not fp32)       */
 } tos_softmax_split;
+/* Either way l sums the rounded P~ that the P~V product consumes, and a separate
+ * unrounded fp32 sum gives lse.  TOS_FP8_E4M3 has no vector form for e4m3
+ * pairs: its rounded sum is always the matrix-unit one, whatever the option. */
 
 /* All-underflow handling (FlashAttention-T section A2, "numerical stability
  * guarantees": an implementation may fall back to per-row computation). */

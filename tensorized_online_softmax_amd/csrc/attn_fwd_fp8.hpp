@@ -1,0 +1,317 @@
+// attn_fwd_fp8.hpp -- the fused attention forward kernel for OCP fp8 e4m3
+// inputs on gfx950 (v_mfma_scale_f32_32x32x64_f8f6f4 for both products).
+//
+// Same method and workgroup shape as the bf16 kernel (8 waves = 256 query
+// rows, 64-key blocks streamed through LDS rings by direct-to-LDS loads, the
+// tensorized online softmax of FlashAttention-T, section A2, Algorithm 1,
+// with the optional per-row fallback of "numerical stability guarantees").
+// What differs for fp8:
+//   * Q, K, V are e4m3 codes with per-tensor fp32 descales; the logit scale
+//     c = scale * log2(e) * q_descale * k_descale, and O is multiplied by
+//     v_descale at the end.
+//   * One MFMA contracts 64 values: S^T = K Q^T takes 2 k-steps per 32-key
+//     tile, O^T += V^T P~^T one instruction per 32-row M tile and 64 keys.
+//   * P~ enters the second product as e4m3, after a 2^8 pre-scale folded
+//     into the exponent (P~ <= 1 becomes <= 256 < 448, and the e4m3 normal
+//     range then starts at P~ = 2^-14).  The fallback threshold tau (default
+//     12) keeps every row's largest term at or above 2^-12.
+//   * As two e4m3 terms: hi = e4m3(2^8 P~) and lo = e4m3(2^8 P~ - hi), each
+//     with its own MFMA.  One e4m3 rounding (3 mantissa bits) alone moves O
+//     by up to 6e-2 and more on rows that average two or three keys (the
+//     oracle's model of it shows this on the stress construction); hi + lo
+//     is within 2^-8 of 2^8 P~.  Values below the e4m3 range still flush to
+//     zero in both terms, so the underflow the fallback guards against is
+//     unchanged.  The kernel is bound by its vector work, so the extra matrix
+//     instructions cost little.
+//   * The row sum that normalises O is the sum of hi + lo that the product
+//     consumes, taken on the matrix unit (an all-ones operand against each
+//     term); the unrounded fp32 sum gives lse.
+//
+// Operand layouts (32x32x64 e4m3, measured on gfx950): slot t of lane half h
+// of the A operand meets slot t of lane half h of the B operand.  So, as in
+// the bf16 kernel, the key order of the P~V contraction is the accumulator
+// order of S^T: slot 16u + r of half h is key 32u + 8(r/4) + 4h + r%4 of the
+// block (tile u, register r), and V's operand is fetched in that order by
+// ds_read_b64_tr_b8 (per 16-lane group, lane j's byte t comes from the
+// address of lane 2t + j/8, at byte offset j%8 of it).
+//
+// LDS rows are 128 bytes (d = 128), 16-byte chunks XOR-swizzled:
+//   K: chunk c of row r at position c ^ (r & 7)
+//   V: chunk c of row r at position c ^ ((r >> 1) & 7)
+// which keeps the K operand reads (8 rows x 16 bytes per 8 lanes) and the
+// transposing V reads (16 rows x 32 bytes per instruction) conflict-free.
+#pragma once
+#include "attn_fwd_kernels.hpp"
+
+namespace tos {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kF8PreScaleLog2 = 8;   // P~ * 2^8 is stored as e4m3
+
+__device__ __forceinline__ f32x16 mfma_f8(i32x8 a, i32x8 b, f32x16 c) {
+  // formats 0/0 = e4m3 for both operands, unit (2^0) block scales
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+template <bool CAUSAL, int X, bool FB_AUTO>
+__global__ __launch_bounds__(kPThreads, 1) void attn_fwd_fp8(FwdArgs a) {
+  constexpr int D = 128;
+  constexpr int RB = D;                       // bytes per K or V row
+  constexpr int BLK = kBc * RB;               // bytes per key block (8 KiB)
+  constexpr int CHW = BLK / 1024 / kPWaves;   // 1 KiB loads per wave per tensor (1)
+  constexpr int NMT = D / 32;                 // 32-row M tiles of O^T
+  constexpr int NV_STEP = 2 * CHW;
+  static_assert(CHW == 1, "one load instruction per wave and tensor");
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kRing * BLK];
+  char* vring = smem;
+
+  const int tid = threadIdx.x, lane = tid & 63, ln = lane & 31, hf = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int bid = blockIdx.x;
+  const int bh = bid % a.BH;
+  const int qb = CAUSAL ? (a.nqb - 1 - bid / a.BH) : bid / a.BH;
+  const int q0 = qb * kPBr;
+  const int N = a.N;
+  const int qrow = q0 + 32 * w + ln;
+  const bool qvalid = qrow < N;
+  const size_t head = (size_t)bh * N * D;
+  const unsigned char* Q = (const unsigned char*)a.q + head;
+  const u32x4 kdesc = buffer_desc((const unsigned char*)a.k + head, (unsigned)N * RB);
+  const u32x4 vdesc = buffer_desc((const unsigned char*)a.v + head, (unsigned)N * RB);
+
+  const int nblk = (N + kBc - 1) / kBc;
+  const int qlast_wg = min(q0 + kPBr, N) - 1;
+  const int jend = CAUSAL ? qlast_wg / kBc + 1 : nblk;
+  const int wq0 = q0 + 32 * w;
+  const int wqlast = min(wq0 + 31, N - 1);
+  const int jend_w = (wq0 >= N) ? 0 : (CAUSAL ? wqlast / kBc + 1 : nblk);
+  const int klim = qvalid ? (CAUSAL ? qrow + 1 : N) : 0;
+
+  // Q^T operand of k-step kk: lane (query ln, half hf) holds Q[qrow][64 kk + 32 hf + 0..31]
+  i32x8 qf[2];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    if (qvalid) {
+      const u32x4* src = (const u32x4*)(Q + (size_t)qrow * D + 64 * kk + 32 * hf);
+      const u32x4 lo = src[0], hi = src[1];
+      qf[kk] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                     (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    } else {
+      qf[kk] = i32x8{};
+    }
+  }
+
+  // direct-to-LDS loads: lane L of wave w fills bytes [1024 w + 16 L, +16) of
+  // the slot = row 8w + L/8, chunk position L%8, fetching the chunk that the
+  // swizzle puts there
+  unsigned kgoff[1], vgoff[1];
+  {
+    const int r = 8 * w + lane / 8, p = lane % 8;
+    kgoff[0] = (unsigned)(r * RB + 16 * (p ^ (r & 7)));
+    vgoff[0] = (unsigned)(r * RB + 16 * (p ^ ((r >> 1) & 7)));
+  }
+  const unsigned lds0 = (unsigned)(unsigned long long)(__attribute__((address_space(3))) char*)smem;
+  const unsigned vdst = lds0 + (unsigned)w * 1024, kdst = vdst + kRing * BLK;
+  auto load_k = [&](int j) {
+    dma_block<CHW>(block_desc(kdesc, j, jend, BLK), kdst + (j % kRing) * BLK, kgoff);
+  };
+  auto load_v = [&](int j) {
+    dma_block<CHW>(block_desc(vdesc, j, jend, BLK), vdst + (j % kRing) * BLK, vgoff);
+  };
+
+  // K operand of tile u, k-step kk: lane (key ln, half hf) reads the 32 bytes
+  // of chunks 4kk + 2hf, +1 of row 32u + ln (the swizzle depends on ln & 7)
+  int koff[2][2];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+    for (int e = 0; e < 2; ++e) koff[kk][e] = kRing * BLK + ln * RB + 16 * ((4 * kk + 2 * hf + e) ^ (ln & 7));
+  // V operand of M tile mt, read c (0..3): lane L addresses row 16c + f(L) at
+  // column 32 mt + g(L): f = 8(t/4) + 4h + t%4 with t = (L%16)/2, h = L/32;
+  // g = 16((L/16)%2) + 8(L%2).  The swizzle of row 16c + f does not depend on c.
+  int voff[NMT];
+  {
+    const int t = (lane % 16) / 2, f = 8 * (t / 4) + 4 * hf + t % 4;
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt)
+      voff[mt] = f * RB + 16 * ((2 * mt + (lane / 16) % 2) ^ ((f >> 1) & 7)) + 8 * (lane % 2);
+  }
+
+  RowState st;
+  row_state_init(st, X == 1);
+  const float c = a.c, tau = a.tau;
+  f32x16 oacc[NMT];
+#pragma unroll
+  for (int mt = 0; mt < NMT; ++mt) oacc[mt] = f32x16{};
+  f32x16 lacc = {};     // row sum of hi + lo of 2^8 P~ (MFMA; every register holds it)
+  float lexact = 0.0f;  // row sum of the unrounded 2^8 P~ (this lane's keys only)
+  const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                      0x38383838, 0x38383838, 0x38383838, 0x38383838};   // e4m3 1.0
+
+  auto kread = [&](int slot, int u, int kk) -> i32x8 {
+    const char* kt = smem + slot * BLK + u * 32 * RB;
+    const u32x4 lo = *(const u32x4*)(kt + koff[kk][0]);
+    const u32x4 hi = *(const u32x4*)(kt + koff[kk][1]);
+    return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                 (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+  };
+  auto vread = [&](int slot, int mt) -> i32x8 {
+    const char* p = vring + slot * BLK + voff[mt];
+    i32x8 r;
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+      const i32x2 x = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+          (__attribute__((address_space(3))) i32x2*)(p + cc * 16 * RB));
+      r[2 * cc] = x[0];
+      r[2 * cc + 1] = x[1];
+    }
+    return r;
+  };
+  // S^T = K_j Q^T into (s0, s1)
+  auto qk = [&](int slot, f32x16& s0, f32x16& s1) {
+    s0 = mfma_f8(kread(slot, 0, 0), qf[0], f32x16{});
+    s1 = mfma_f8(kread(slot, 1, 0), qf[0], f32x16{});
+    s0 = mfma_f8(kread(slot, 0, 1), qf[1], s0);
+    s1 = mfma_f8(kread(slot, 1, 1), qf[1], s1);
+  };
+  // O^T += V_j^T (hi + lo)^T, and the row sum of hi + lo (ones x (hi + lo)^T)
+  auto pv = [&](int slot, const i32x8& hi, const i32x8& lo) {
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) {
+      const i32x8 vop = vread(slot, mt);
+      oacc[mt] = mfma_f8(vop, hi, oacc[mt]);
+      oacc[mt] = mfma_f8(vop, lo, oacc[mt]);
+    }
+    lacc = mfma_f8(ones, hi, lacc);
+    lacc = mfma_f8(ones, lo, lacc);
+  };
+
+  // ---- the softmax of one key block (Algorithm 1)
+  auto block_state = [&](int j, f32x16& s0, f32x16& s1, float& alpha, float& nb) {
+    if (j == jend_w - 1) {
+      // key of register r of tile u: j*Bc + 32u + 8(r/4) + 4hf + r%4
+      const int kb = j * kBc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = kb + 8 * (r / 4) + 4 * hf + (r % 4);
+        if (key >= klim) s0[r] = -__builtin_inff();
+        if (key + 32 >= klim) s1[r] = -__builtin_inff();
+      }
+    }
+    float m4[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f32x16& sv = (q / 2) ? s1 : s0;
+      const int r0 = 8 * (q % 2);
+      float m = fmax_raw(sv[r0], sv[r0 + 1]);
+#pragma unroll
+      for (int r = r0 + 2; r < r0 + 8; r += 2) m = fmax_raw(m, fmax_raw(sv[r], sv[r + 1]));
+      m4[q] = m;
+    }
+    float bm = fmax_raw(fmax_raw(m4[0], m4[1]), fmax_raw(m4[2], m4[3]));
+    bm = qvalid ? bm : -__builtin_inff();
+    row_max_update(st, bm);
+    alpha = ref_advance(st, block_ref<X, FB_AUTO>(st, c, tau), c);
+    // the 2^8 pre-scale rides on the exponent
+    nb = neg_c_ref(st, c) + (float)kF8PreScaleLog2;
+  };
+  // steps 4-7: 2^8 P~ = exp2(c*S - c*ref + 8), packed to e4m3 as hi and lo,
+  // unrounded row sum
+  auto exps = [&](const f32x16& s0, const f32x16& s1, i32x8& pk, i32x8& pl, float alpha, float nb) {
+    float pe0 = 0.0f, pe1 = 0.0f;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const f32x16& sv = u ? s1 : s0;
+#pragma unroll
+      for (int r = 0; r < 16; r += 4) {
+        float p[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r + e], c, nb));
+          if (u) pe1 += p[e]; else pe0 += p[e];
+        }
+        // operand bytes 16u + r .. +3 = dword 4u + r/4: low word, then high word
+        int wd = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+        wd = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], wd, true);
+        pk[4 * u + r / 4] = wd;
+        const auto h01 = __builtin_amdgcn_cvt_pk_f32_fp8(wd, false);
+        const auto h23 = __builtin_amdgcn_cvt_pk_f32_fp8(wd, true);
+        int wl = __builtin_amdgcn_cvt_pk_fp8_f32(p[0] - h01[0], p[1] - h01[1], 0, false);
+        wl = __builtin_amdgcn_cvt_pk_fp8_f32(p[2] - h23[0], p[3] - h23[1], wl, true);
+        pl[4 * u + r / 4] = wl;
+      }
+    }
+    lexact = lexact * alpha + (pe0 + pe1);
+  };
+  auto rescale = [&](float alpha) {
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt) oacc[mt] *= alpha;
+      lacc *= alpha;
+    }
+  };
+
+  // ---- prologue: K_0..K_3 and V_0, V_1 into the rings, then S_0 and its state
+#pragma unroll
+  for (int j = 0; j < kKAhead; ++j) load_k(j);
+#pragma unroll
+  for (int j = 0; j < kVAhead; ++j) load_v(j);
+  step_barrier<0>();
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0), as the compiler sees it (Q loaded)
+
+  // Entering step j: S_j in (s0, s1), P~_{j-1} in pp, alpha_j / -c ref_j + 8 in
+  // alpha_cur / nb_cur.  Step j: exponentials of S_j, S_{j+1} = K_{j+1} Q^T,
+  // P~_{j-1} V_{j-1}, the state of S_{j+1}; O *= alpha_j at its end.
+  f32x16 s0 = {}, s1 = {};
+  i32x8 pp = {}, pc = {}, lp = {}, lc = {};   // hi and lo terms of P~_{j-1}, P~_j
+  float alpha_cur = 1.0f, nb_cur = 0.0f, alpha_nxt = 1.0f, nb_nxt = 0.0f;
+  if (jend_w > 0) {
+    qk(0, s0, s1);
+    block_state(0, s0, s1, alpha_cur, nb_cur);
+  }
+  step_barrier<0>();   // step 0 refills K_0's slot
+
+  for (int j = 0; j <= jend; ++j) {
+    load_k(j + kKAhead);
+    load_v(j + kVAhead);
+    if (j < jend_w) exps(s0, s1, pc, lc, alpha_cur, nb_cur);
+    if (j + 1 < jend_w) qk((j + 1) % kRing, s0, s1);
+    if (j >= 1 && j <= jend_w) pv((j - 1) % kRing, pp, lp);
+    if (j + 1 < jend_w) block_state(j + 1, s0, s1, alpha_nxt, nb_nxt);
+    step_barrier<2 * NV_STEP>();
+    if (j < jend_w) rescale(alpha_cur);
+    alpha_cur = alpha_nxt;
+    nb_cur = nb_nxt;
+    pp = pc;
+    lp = lc;
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  // ---- epilogue: O / l (l: the sum of hi + lo, so the 2^8 cancels), and
+  // lse = lse_scale * ref + ln(l_exact / 2^8)
+  const float l = lacc[0];
+  const float le = pair_reduce(lexact, [](float x, float y) { return x + y; });
+  const float inv = l > 0.0f ? a.o_scale / l : 0.0f;
+  if (qvalid) {
+    __bf16* O = (__bf16*)a.o + head + (size_t)qrow * D;
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        bf16x4 ov;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) ov[u] = (__bf16)(oacc[mt][4 * g + u] * inv);
+        *(bf16x4*)(O + 32 * mt + 8 * g + 4 * hf) = ov;
+      }
+    }
+    if (a.lse != nullptr && hf == 0)
+      a.lse[(size_t)bh * N + qrow] =
+          le > 0.0f ? a.lse_scale * st.ref + (__logf(le) - (float)kF8PreScaleLog2 * 0.69314718f)
+                    : -__builtin_inff();
+  }
+  count_tiles<X, FB_AUTO>(a, st, lane, qrow);
+}
+
+}  // namespace tos

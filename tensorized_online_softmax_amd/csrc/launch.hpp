@@ -10,7 +10,7 @@ struct KernelChoice {
   int d;             // 64 or 128
   bool causal;
   int x;             // 1, 16 or 32
-  bool rowsum_mfma;  // row sum on the matrix unit
+  bool rowsum_mfma;  // row sum on the matrix unit (fp8: always)
   bool fb_auto;      // fallback AUTO (x > 1 only)
 };
 
@@ -18,5 +18,6 @@ struct KernelChoice {
 // instance, or the launch error.
 hipError_t launch_bf16(const FwdArgs& a, const KernelChoice& k, hipStream_t stream);
 hipError_t launch_f32(const FwdArgs& a, const KernelChoice& k, hipStream_t stream);
+hipError_t launch_fp8(const FwdArgs& a, const KernelChoice& k, hipStream_t stream);
 
 }  // namespace tos

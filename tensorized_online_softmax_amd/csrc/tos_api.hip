@@ -127,7 +127,7 @@ tos_status tos_attn_fwd(const void* q, const void* k, const void* v, void* o, fl
   kc.x = op.fallback == TOS_FALLBACK_FORCE ? 1 : op.x_tile;
   kc.fb_auto = op.fallback == TOS_FALLBACK_AUTO && op.x_tile > 1;
   if (dtype == TOS_F32 && kc.rowsum_mfma) return TOS_ERR_UNSUPPORTED;
-  if (dtype == TOS_FP8_E4M3) return TOS_ERR_UNSUPPORTED;
+  if (dtype == TOS_FP8_E4M3 && d != 128) return TOS_ERR_UNSUPPORTED;
 
   tos::FwdArgs a;
   a.q = q;
@@ -138,10 +138,15 @@ tos_status tos_attn_fwd(const void* q, const void* k, const void* v, void* o, fl
   a.BH = (int)BH;
   a.N = (int)N;
   a.nqb = (int)nqb;
-  a.lse_scale = scale;
-  a.c = (float)((double)scale * kLog2e);
-  a.o_scale = 1.0f;
-  a.tau = op.fallback_tau > 0.0f ? op.fallback_tau : 100.0f;
+  // fp8: the stored codes times their descales are the real values, so the
+  // logit scale takes q_descale * k_descale and O takes v_descale
+  const double qk_descale = dtype == TOS_FP8_E4M3 ? (double)op.q_descale * (double)op.k_descale : 1.0;
+  a.lse_scale = (float)((double)scale * qk_descale);
+  a.c = (float)((double)scale * qk_descale * kLog2e);
+  a.o_scale = dtype == TOS_FP8_E4M3 ? op.v_descale : 1.0f;
+  // default thresholds: bf16/fp32 P~ keep 2^-100 far above their underflow;
+  // e4m3 P~ (pre-scaled by 2^8) keeps every row's largest term >= 2^-12
+  a.tau = op.fallback_tau > 0.0f ? op.fallback_tau : (dtype == TOS_FP8_E4M3 ? 12.0f : 100.0f);
   a.fallback_tiles = op.fallback_tiles;
   // FORCE runs the per-row kernel and counts every X-row tile of the request
   a.count_x = op.fallback == TOS_FALLBACK_FORCE ? op.x_tile : 0;
@@ -153,6 +158,8 @@ tos_status tos_attn_fwd(const void* q, const void* k, const void* v, void* o, fl
     e = tos::launch_bf16(a, kc, s);
   else if (dtype == TOS_F32)
     e = tos::launch_f32(a, kc, s);
+  else
+    e = tos::launch_fp8(a, kc, s);
   if (log_enabled())
     std::fprintf(stderr, "[tos] dtype=%d B=%lld H=%lld N=%lld d=%d causal=%d X=%d rowsum_mfma=%d "
                  "fallback=%d grid=%lld: %s\n", (int)dtype, (long long)B, (long long)H,

@@ -41,6 +41,7 @@ class Workload:
     std: float = 1.0      # standard deviation of the Q and K draws
     spike_frac: float = 0.0     # fraction of query rows that get one spiked key
     spike_logit: float = 0.0    # logit offset (in scaled units) of the spiked key
+    fallback: str = "off"       # all-underflow fallback the workload runs with
     note: str = field(default="", compare=False)
 
     @property
@@ -62,7 +63,7 @@ WORKLOADS = {
     "long_causal_bf16": Workload("long_causal_bf16", 1, 16, 16384, 128, "bf16", True, 32, 4000,
                                  note="long-sequence causal, bf16, d=128, N=16384"),
     "fp8_spiky": Workload("fp8_spiky", 1, 16, 8192, 128, "fp8", False, 32, 5000,
-                          std=math.sqrt(8.0), spike_frac=0.2, spike_logit=40.0,
+                          std=math.sqrt(8.0), spike_frac=0.2, spike_logit=40.0, fallback="auto",
                           note="fp8 e4m3 stress: logit std 8, 20% of rows with one +40 key"),
 }
 
