@@ -25,21 +25,29 @@ sys.path.insert(0, ROOT)
 
 PEAK_TFLOPS = {"bf16": 2516.6, "fp8": 5033.2, "f32": 157.3}   # MI355X dense MFMA
 HBM_GBPS = 8000.0
-KERNEL_SOURCES = ["tensorized_online_softmax_amd/csrc/attn_fwd_kernels.hpp",
-                  "tensorized_online_softmax_amd/csrc/attn_fwd_fp8.hpp",
-                  "tensorized_online_softmax_amd/csrc/softmax_tile.hpp"]
+# sources of each dtype's kernel: a committed traffic summary is used only
+# while these are unchanged
+KERNEL_SOURCES = {
+    "bf16": ["tensorized_online_softmax_amd/csrc/attn_fwd_kernels.hpp",
+             "tensorized_online_softmax_amd/csrc/softmax_tile.hpp"],
+    "f32": ["tensorized_online_softmax_amd/csrc/attn_fwd_kernels.hpp",
+            "tensorized_online_softmax_amd/csrc/softmax_tile.hpp"],
+    "fp8": ["tensorized_online_softmax_amd/csrc/attn_fwd_kernels.hpp",
+            "tensorized_online_softmax_amd/csrc/attn_fwd_fp8.hpp",
+            "tensorized_online_softmax_amd/csrc/softmax_tile.hpp"],
+}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_{workload}.txt")
 
 
-def kernel_hash():
+def kernel_hash(dtype):
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in KERNEL_SOURCES[dtype]:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def read_traffic(workload):
+def read_traffic(workload, dtype):
     """HBM bytes per launch from the committed counter summary, or None when
     there is none or the kernel sources changed since it was taken."""
     path = TRAFFIC_FILE.format(workload=workload)
@@ -50,7 +58,7 @@ def read_traffic(workload):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip()
-    if vals.get("kernel_sources_sha256_16") != kernel_hash():
+    if vals.get("kernel_sources_sha256_16") != kernel_hash(dtype):
         return None
     try:
         return float(vals["hbm_bytes_per_launch"])
@@ -88,6 +96,34 @@ def cpu_baseline(w, inp, target_rows):
                       f"attention (oracle_attn_exact), {dt:.1f} s"}
 
 
+def mfma_ceiling():
+    """Dense bf16 GEMM throughput of the vendor library (torch.matmul) on this
+    GPU: the practical MFMA ceiling that the published peak overstates when the
+    data are random (power-limited clock)."""
+    import torch
+    torch.cuda.set_device(0)
+    out = {"metric": "bf16 GEMM TFLOP/s (torch.matmul), context for the MFMA roofline",
+           "unit": "TFLOP/s", "peak_published": PEAK_TFLOPS["bf16"], "runs": []}
+    for n, data in ((8192, "randn"), (16384, "randn"), (8192, "zeros")):
+        make = torch.randn if data == "randn" else torch.zeros
+        a = make(n, n, device="cuda", dtype=torch.bfloat16)
+        b = make(n, n, device="cuda", dtype=torch.bfloat16)
+        for _ in range(5):
+            a @ b
+        torch.cuda.synchronize()
+        it = 20 if n <= 8192 else 6
+        t0 = time.perf_counter()
+        for _ in range(it):
+            a @ b
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / it
+        tf = 2.0 * n ** 3 / dt / 1e12
+        out["runs"].append({"m=n=k": n, "data": data, "tflops": round(tf, 1),
+                            "frac_of_published_peak": round(tf / PEAK_TFLOPS["bf16"], 4)})
+        print(f"[bench] bf16 GEMM {n}^3 {data}: {tf:.0f} TFLOP/s", file=sys.stderr, flush=True)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -101,7 +137,14 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=0, help="0 = every row")
     ap.add_argument("--copy-calib-mib", type=int, default=0)
+    ap.add_argument("--mfma-ceiling", action="store_true",
+                    help="instead of the attention bench: time torch's bf16 GEMM (the vendor "
+                         "library) on random and on all-zero data, for the MFMA throughput this "
+                         "GPU sustains under its power limit")
     args = ap.parse_args()
+    if args.mfma_ceiling:
+        mfma_ceiling()
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(heads shard across GPUs with no exchange; see the design notes). "
@@ -165,7 +208,7 @@ def main():
     peak = PEAK_TFLOPS[w.dtype]
     achieved = flops / avg_launch_s / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(achieved / peak, 4), "traffic": read_traffic(w.name)}
+                "frac": round(achieved / peak, 4), "traffic": read_traffic(w.name, w.dtype)}
     result = {
         "metric": "fused attention fwd TFLOP/s at 1 GPU and % of MFMA peak (bf16, fp8)",
         "value": round(flops / (ms_per_step / 1e3) / 1e12, 2),

@@ -425,85 +425,73 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_bf16(FwdArgs a) {
   // loads) are complete from here on, so no wait for them lands in the loop
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0), expcnt and lgkmcnt untouched
 
-  // Pipeline of key block b: S_b = K_b Q^T and its tile maximum in step b-1,
-  // its exponentials and row sums in step b, P~_b V_b in step b+1; O is
-  // rescaled by alpha_b at the end of step b (after P~_{b-1} V_{b-1}, before
-  // P~_b V_b).  Entering step j: S_j (masked if it is the wave's last block)
-  // in S[0], P~_{j-1} in P[1], alpha_j and -c ref_j in alpha_cur, nb_cur.
+  // Pipeline of key block b: S_b = K_b Q^T in step b-1; its tile maximum,
+  // exponentials and row sums in step b, where O is rescaled by alpha_b at the
+  // end (after P~_{b-1} V_{b-1}, before P~_b V_b); P~_b V_b in step b+1.
+  // Entering step j: S_j in S[0], P~_{j-1} in P[1].
   f32x16 S[2][2];
   bf16x8 P[2][4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) P[0][t] = P[1][t] = bf16x8{};
   S[0][0] = S[0][1] = S[1][0] = S[1][1] = f32x16{};
-  float alpha_cur = 1.0f, nb_cur = 0.0f, alpha_nxt = 1.0f, nb_nxt = 0.0f;
-  // whole-block softmax state (tile maximum and reference) of S_j in (s0, s1)
-  auto block_state = [&](int j, f32x16& s0, f32x16& s1, float& alpha, float& nb) {
-    if (j == jend_w - 1) mask_block(j, s0, s1);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) max_part(q, s0, s1);
-    max_combine();
-    tile_ref();
-    advance(alpha, nb);
-  };
-  if (jend_w > 0) {
-    qk(0, S[0][0], S[0][1]);
-    block_state(0, S[0][0], S[0][1], alpha_cur, nb_cur);
-  }
+  if (jend_w > 0) qk(0, S[0][0], S[0][1]);
   // step 0 refills K_0's slot: every wave must be done reading it
   step_barrier<0>();
 
   // Any step (first, last, idle), slots and masking decided at run time.
   auto edge_step = [&](int j) {
     step_loads(j);
+    float alpha = 1.0f, nb = 0.0f;
     if (j < jend_w) {
+      if (j == jend_w - 1) mask_block(j, S[0][0], S[0][1]);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) max_part(q, S[0][0], S[0][1]);
+      max_combine();
+      tile_ref();
+      advance(alpha, nb);
       sums_reset();
 #pragma unroll
-      for (int k = 0; k < 16; ++k) exp_unit(k, S[0][0], S[0][1], P[0], nb_cur);
-      sums_commit(alpha_cur);
+      for (int k = 0; k < 16; ++k) exp_unit(k, S[0][0], S[0][1], P[0], nb);
+      sums_commit(alpha);
     }
     if (j + 1 < jend_w) qk((j + 1) % kRing, S[0][0], S[0][1]);
     if (j >= 1 && j <= jend_w) pv((j - 1) % kRing, P[1]);
-    if (j + 1 < jend_w) block_state(j + 1, S[0][0], S[0][1], alpha_nxt, nb_nxt);
     step_barrier<2 * NV_STEP>();
-    if (j < jend_w) rescale(alpha_cur);
-    alpha_cur = alpha_nxt;
-    nb_cur = nb_nxt;
+    if (j < jend_w) rescale(alpha);
 #pragma unroll
     for (int t = 0; t < 4; ++t) P[1][t] = P[0][t];
   };
 
-  // Steady step j = 1 + 4g + u (u = 0..3): j >= 1 and S_{j+1} is not the
-  // wave's last block.  Two phases of one straight-line block, each a run of
-  // chunks of one matrix instruction and a share of the vector work:
-  //   A: S_{j+1} = K_{j+1} Q^T          with the exponentials of S_j (part)
-  //   B: O^T += V_{j-1}^T P~_{j-1}^T    with the tile maximum of S_{j+1} and
-  //                                     the rest of the exponentials of S_j
-  // Operand reads run three instructions ahead.  S and P~ alternate between
-  // the two register sets.
-  // Vector work per chunk, spread evenly (two waves share a SIMD and run the
-  // same chunk at about the same time, so the even spread suits both):
-  //   phase A: exponential units 0..EA-1, unit k in chunk k*NQK/EA
-  //   phase B: the tile-maximum chain of S_{j+1} in its first chunks (d=128:
-  //            parts 0-1 | 2-3 | combine | tile max | advance; d=64: parts
-  //            0-3 | combine, tile max | advance), then units EA..15 spread
-  //            over the chunks after it
-  constexpr int EA = NQK >= 16 ? 10 : 8;       // exponential units in phase A
-  constexpr int MAXC = NPV >= 16 ? 5 : 3;      // phase-B chunks of the maximum chain
+  // Steady step j = 1 + 4g + u (u = 0..3): j >= 1 and S_j is not the wave's
+  // last block.  Two phases of one straight-line block, each a run of chunks
+  // of one matrix instruction and a share of the vector work on S_j:
+  //   A: S_{j+1} = K_{j+1} Q^T          with the tile-maximum chain of S_j
+  //                                     (computed a step ago: no wait), then
+  //                                     the first EA exponential units
+  //   B: O^T += V_{j-1}^T P~_{j-1}^T    with the remaining units (no
+  //                                     dependency chain left to wait on)
+  // The chain (d=128: parts 0-1 | 2-3 | combine | tile max | advance; d=64:
+  // parts 0-3 | combine, tile max | advance) takes the first chunks of A;
+  // units are spread evenly over the chunks after it and over B.  Operand
+  // reads run LA instructions ahead; S and P~ alternate between the two
+  // register sets.
+  constexpr int MAXC = NQK >= 16 ? 5 : 3;      // phase-A chunks of the maximum chain
+  constexpr int EA = NQK >= 16 ? 6 : 3;        // exponential units in phase A
   constexpr int LA = 3;                        // operand read lookahead
-  auto max_chunk = [&](int i, f32x16& n0, f32x16& n1) {
-    if constexpr (NPV >= 16) {
-      if (i == 0) { max_part(0, n0, n1); max_part(1, n0, n1); }
-      if (i == 1) { max_part(2, n0, n1); max_part(3, n0, n1); }
+  auto max_chunk = [&](int i, f32x16& c0, f32x16& c1, float& alpha, float& nb) {
+    if constexpr (NQK >= 16) {
+      if (i == 0) { max_part(0, c0, c1); max_part(1, c0, c1); }
+      if (i == 1) { max_part(2, c0, c1); max_part(3, c0, c1); }
       if (i == 2) max_combine();
       if (i == 3) tile_ref();
-      if (i == 4) advance(alpha_nxt, nb_nxt);
+      if (i == 4) advance(alpha, nb);
     } else {
       if (i == 0) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) max_part(q, n0, n1);
+        for (int q = 0; q < 4; ++q) max_part(q, c0, c1);
       }
       if (i == 1) { max_combine(); tile_ref(); }
-      if (i == 2) advance(alpha_nxt, nb_nxt);
+      if (i == 2) advance(alpha, nb);
     }
   };
   auto steady_step = [&](auto U, int j) {
@@ -516,33 +504,33 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_bf16(FwdArgs a) {
     bf16x8 kop[LA], vop[LA];
 #pragma unroll
     for (int g = 0; g < LA; ++g) kop[g] = kread(kt, g);
+    float alpha = 1.0f, nb = 0.0f;
     sums_reset();
-    // phase A
+    // phase A: units 0..EA-1 in the chunks after the chain
 #pragma unroll
     for (int g = 0; g < NQK; ++g) {
       const bf16x8 av = kop[g % LA];
       if (g + LA < NQK) kop[g % LA] = kread(kt, g + LA);
       else vop[(g + LA - NQK) % LA] = vread(vt, g + LA - NQK);
       qk_mfma(g, av, n0, n1);
+      max_chunk(g, c0, c1, alpha, nb);
 #pragma unroll
       for (int k = 0; k < EA; ++k)
-        if (k * NQK / EA == g) exp_unit(k, c0, c1, P[cur], nb_cur);
+        if (MAXC + k * (NQK - MAXC) / EA == g) exp_unit(k, c0, c1, P[cur], nb);
       __builtin_amdgcn_sched_barrier(0);
     }
-    // phase B
+    // phase B: units EA..15 spread over the chunks
 #pragma unroll
     for (int i = 0; i < NPV; ++i) {
       const bf16x8 av = vop[i % LA];
       if (i + LA < NPV) vop[i % LA] = vread(vt, i + LA);
       pv_mfma(i, av, P[nxt]);
-      max_chunk(i, n0, n1);
 #pragma unroll
       for (int k = EA; k < 16; ++k)
-        if (MAXC - 1 + (k - EA + 1) * (NPV - MAXC + 1) / (16 - EA + 1) == i)
-          exp_unit(k, c0, c1, P[cur], nb_cur);
+        if ((k - EA) * NPV / (16 - EA) == i) exp_unit(k, c0, c1, P[cur], nb);
       __builtin_amdgcn_sched_barrier(0);
     }
-    sums_commit(alpha_cur);
+    sums_commit(alpha);
     pin(P[cur][0]);
     pin(P[cur][1]);
     pin(P[cur][2]);
@@ -550,14 +538,12 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_bf16(FwdArgs a) {
     pin(lexact);
     if constexpr (!ROWSUM_MFMA) pin(lsum);
     step_barrier<2 * NV_STEP>();
-    rescale(alpha_cur);
-    alpha_cur = alpha_nxt;
-    nb_cur = nb_nxt;
+    rescale(alpha);
   };
 
   int j = 0;
   edge_step(j++);
-  for (; j + 5 < jend_w; j += 4) {
+  for (; j + 4 < jend_w; j += 4) {
     steady_step(Int<0>(), j);
     steady_step(Int<1>(), j + 1);
     steady_step(Int<2>(), j + 2);
