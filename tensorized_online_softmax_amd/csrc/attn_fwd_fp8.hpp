@@ -188,62 +188,59 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_fp8(FwdArgs a) {
     lacc = mfma_f8(ones, lo, lacc);
   };
 
-  // ---- the softmax of one key block (Algorithm 1)
-  auto block_state = [&](int j, f32x16& s0, f32x16& s1, float& alpha, float& nb) {
-    if (j == jend_w - 1) {
-      // key of register r of tile u: j*Bc + 32u + 8(r/4) + 4hf + r%4
-      const int kb = j * kBc;
+  // ---- the softmax of one key block (Algorithm 1), in pieces
+  // key of register r of tile u in block j: j*Bc + 32u + 8(r/4) + 4hf + r%4
+  auto mask_block = [&](int j, f32x16& s0, f32x16& s1) {
+    const int kb = j * kBc;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = kb + 8 * (r / 4) + 4 * hf + (r % 4);
-        if (key >= klim) s0[r] = -__builtin_inff();
-        if (key + 32 >= klim) s1[r] = -__builtin_inff();
-      }
+    for (int r = 0; r < 16; ++r) {
+      const int key = kb + 8 * (r / 4) + 4 * hf + (r % 4);
+      if (key >= klim) s0[r] = -__builtin_inff();
+      if (key + 32 >= klim) s1[r] = -__builtin_inff();
     }
-    float m4[4];
+  };
+  float m4[4];
+  auto max_part = [&](int q, const f32x16& s0, const f32x16& s1) {
+    const f32x16& sv = (q / 2) ? s1 : s0;
+    const int r0 = 8 * (q % 2);
+    float m = fmax_raw(sv[r0], sv[r0 + 1]);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const f32x16& sv = (q / 2) ? s1 : s0;
-      const int r0 = 8 * (q % 2);
-      float m = fmax_raw(sv[r0], sv[r0 + 1]);
-#pragma unroll
-      for (int r = r0 + 2; r < r0 + 8; r += 2) m = fmax_raw(m, fmax_raw(sv[r], sv[r + 1]));
-      m4[q] = m;
-    }
+    for (int r = r0 + 2; r < r0 + 8; r += 2) m = fmax_raw(m, fmax_raw(sv[r], sv[r + 1]));
+    m4[q] = m;
+  };
+  float ref_new = 0.0f;
+  auto max_combine = [&]() {
     float bm = fmax_raw(fmax_raw(m4[0], m4[1]), fmax_raw(m4[2], m4[3]));
     bm = qvalid ? bm : -__builtin_inff();
     row_max_update(st, bm);
-    alpha = ref_advance(st, block_ref<X, FB_AUTO>(st, c, tau), c);
-    // the 2^8 pre-scale rides on the exponent
+  };
+  auto tile_ref = [&]() { ref_new = block_ref<X, FB_AUTO>(st, c, tau); };
+  // alpha, and -c*ref + 8: the 2^8 pre-scale rides on the exponent
+  auto advance = [&](float& alpha, float& nb) {
+    alpha = ref_advance(st, ref_new, c);
     nb = neg_c_ref(st, c) + (float)kF8PreScaleLog2;
   };
-  // steps 4-7: 2^8 P~ = exp2(c*S - c*ref + 8), packed to e4m3 as hi and lo,
-  // unrounded row sum
-  auto exps = [&](const f32x16& s0, const f32x16& s1, i32x8& pk, i32x8& pl, float alpha, float nb) {
-    float pe0 = 0.0f, pe1 = 0.0f;
+  // steps 4-7 for registers r..r+3 of tile u (unit k: u = k / 4, r = 4 (k % 4)):
+  // 2^8 P~ = exp2(c*S - c*ref + 8) as hi + lo e4m3 terms (operand dword 4u + r/4),
+  // and the unrounded row sum
+  float pe[2];
+  auto exp_unit = [&](int k, const f32x16& s0, const f32x16& s1, i32x8& pk, i32x8& pl, float nb) {
+    const int u = k / 4, r = 4 * (k % 4);
+    const f32x16& sv = u ? s1 : s0;
+    float p[4];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const f32x16& sv = u ? s1 : s0;
-#pragma unroll
-      for (int r = 0; r < 16; r += 4) {
-        float p[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r + e], c, nb));
-          if (u) pe1 += p[e]; else pe0 += p[e];
-        }
-        // operand bytes 16u + r .. +3 = dword 4u + r/4: low word, then high word
-        int wd = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
-        wd = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], wd, true);
-        pk[4 * u + r / 4] = wd;
-        const auto h01 = __builtin_amdgcn_cvt_pk_f32_fp8(wd, false);
-        const auto h23 = __builtin_amdgcn_cvt_pk_f32_fp8(wd, true);
-        int wl = __builtin_amdgcn_cvt_pk_fp8_f32(p[0] - h01[0], p[1] - h01[1], 0, false);
-        wl = __builtin_amdgcn_cvt_pk_fp8_f32(p[2] - h23[0], p[3] - h23[1], wl, true);
-        pl[4 * u + r / 4] = wl;
-      }
+    for (int e = 0; e < 4; ++e) {
+      p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r + e], c, nb));
+      pe[u] += p[e];
     }
-    lexact = lexact * alpha + (pe0 + pe1);
+    int wd = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+    wd = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], wd, true);
+    pk[4 * u + r / 4] = wd;
+    const auto h01 = __builtin_amdgcn_cvt_pk_f32_fp8(wd, false);
+    const auto h23 = __builtin_amdgcn_cvt_pk_f32_fp8(wd, true);
+    int wl = __builtin_amdgcn_cvt_pk_fp8_f32(p[0] - h01[0], p[1] - h01[1], 0, false);
+    wl = __builtin_amdgcn_cvt_pk_fp8_f32(p[2] - h23[0], p[3] - h23[1], wl, true);
+    pl[4 * u + r / 4] = wl;
   };
   auto rescale = [&](float alpha) {
     if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
@@ -252,8 +249,12 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_fp8(FwdArgs a) {
       lacc *= alpha;
     }
   };
+  auto step_loads = [&](int j) {
+    load_k(j + kKAhead);
+    load_v(j + kVAhead);
+  };
 
-  // ---- prologue: K_0..K_3 and V_0, V_1 into the rings, then S_0 and its state
+  // ---- prologue: K_0..K_3 and V_0, V_1 into the rings, then S_0
 #pragma unroll
   for (int j = 0; j < kKAhead; ++j) load_k(j);
 #pragma unroll
@@ -261,32 +262,107 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_fp8(FwdArgs a) {
   step_barrier<0>();
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0), as the compiler sees it (Q loaded)
 
-  // Entering step j: S_j in (s0, s1), P~_{j-1} in pp, alpha_j / -c ref_j + 8 in
-  // alpha_cur / nb_cur.  Step j: exponentials of S_j, S_{j+1} = K_{j+1} Q^T,
-  // P~_{j-1} V_{j-1}, the state of S_{j+1}; O *= alpha_j at its end.
-  f32x16 s0 = {}, s1 = {};
-  i32x8 pp = {}, pc = {}, lp = {}, lc = {};   // hi and lo terms of P~_{j-1}, P~_j
-  float alpha_cur = 1.0f, nb_cur = 0.0f, alpha_nxt = 1.0f, nb_nxt = 0.0f;
-  if (jend_w > 0) {
-    qk(0, s0, s1);
-    block_state(0, s0, s1, alpha_cur, nb_cur);
-  }
+  // Pipeline of key block b (as in the bf16 kernel): S_b = K_b Q^T in step b-1;
+  // its tile maximum, exponentials and row sums in step b, where O is rescaled
+  // by alpha_b at the end; P~_b V_b in step b+1.  Entering step j: S_j in S[0],
+  // the hi and lo terms of P~_{j-1} in PH[1], PL[1].
+  f32x16 S[2][2];
+  i32x8 PH[2], PL[2];
+  S[0][0] = S[0][1] = S[1][0] = S[1][1] = f32x16{};
+  PH[0] = PH[1] = PL[0] = PL[1] = i32x8{};
+  if (jend_w > 0) qk(0, S[0][0], S[0][1]);
   step_barrier<0>();   // step 0 refills K_0's slot
 
-  for (int j = 0; j <= jend; ++j) {
-    load_k(j + kKAhead);
-    load_v(j + kVAhead);
-    if (j < jend_w) exps(s0, s1, pc, lc, alpha_cur, nb_cur);
-    if (j + 1 < jend_w) qk((j + 1) % kRing, s0, s1);
-    if (j >= 1 && j <= jend_w) pv((j - 1) % kRing, pp, lp);
-    if (j + 1 < jend_w) block_state(j + 1, s0, s1, alpha_nxt, nb_nxt);
+  auto edge_step = [&](int j) {
+    step_loads(j);
+    float alpha = 1.0f, nb = 0.0f;
+    if (j < jend_w) {
+      if (j == jend_w - 1) mask_block(j, S[0][0], S[0][1]);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) max_part(q, S[0][0], S[0][1]);
+      max_combine();
+      tile_ref();
+      advance(alpha, nb);
+      pe[0] = pe[1] = 0.0f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) exp_unit(k, S[0][0], S[0][1], PH[0], PL[0], nb);
+      lexact = lexact * alpha + (pe[0] + pe[1]);
+    }
+    if (j + 1 < jend_w) qk((j + 1) % kRing, S[0][0], S[0][1]);
+    if (j >= 1 && j <= jend_w) pv((j - 1) % kRing, PH[1], PL[1]);
     step_barrier<2 * NV_STEP>();
-    if (j < jend_w) rescale(alpha_cur);
-    alpha_cur = alpha_nxt;
-    nb_cur = nb_nxt;
-    pp = pc;
-    lp = lc;
+    if (j < jend_w) rescale(alpha);
+    PH[1] = PH[0];
+    PL[1] = PL[0];
+  };
+
+  // Steady step j = 1 + 4g + u: j >= 1 and S_j is not the wave's last block.
+  // One straight-line block of matrix-instruction chunks:
+  //   A (4 chunks): S_{j+1} = K_{j+1} Q^T, each with a part of the tile-maximum
+  //                 chain of S_j (parts 0-1 | 2-3 | combine + tile max | advance)
+  //   B (10 chunks): O^T += V_{j-1}^T (hi + lo)^T and the row sum of P~_{j-1},
+  //                 with the 8 exponential units of S_j in the first 8
+  // Constant ring slots (four steps per loop iteration); S and P~ alternate
+  // between the two register sets.
+  auto steady_step = [&](auto U, int j) {
+    constexpr int u = decltype(U)::value;
+    constexpr int cur = u & 1, nxt = cur ^ 1;
+    constexpr int kslot = (u + 2) % kRing, vslot = u % kRing;   // K_{j+1}, V_{j-1}
+    f32x16 &c0 = S[cur][0], &c1 = S[cur][1], &n0 = S[nxt][0], &n1 = S[nxt][1];
+    step_loads(j);
+    float alpha = 1.0f, nb = 0.0f;
+    pe[0] = pe[1] = 0.0f;
+    // phase A: QK g = 2 kk + t, operands read one instruction ahead
+    i32x8 kop = kread(kslot, 0, 0);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const i32x8 av = kop;
+      if (g + 1 < 4) kop = kread(kslot, (g + 1) % 2, (g + 1) / 2);
+      f32x16& acc = (g % 2) ? n1 : n0;
+      acc = mfma_f8(av, qf[g / 2], g < 2 ? f32x16{} : acc);
+      if (g == 0) { max_part(0, c0, c1); max_part(1, c0, c1); }
+      if (g == 1) { max_part(2, c0, c1); max_part(3, c0, c1); }
+      if (g == 2) { max_combine(); tile_ref(); }
+      if (g == 3) advance(alpha, nb);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // phase B: per M tile one V operand for the hi and the lo product
+    i32x8 vop = vread(vslot, 0), vop_hold = {};
+#pragma unroll
+    for (int i = 0; i < 2 * NMT + 2; ++i) {
+      if (i < 2 * NMT) {
+        const int mt = i / 2;
+        if (i % 2 == 0) {
+          const i32x8 av = vop;
+          if (mt + 1 < NMT) vop = vread(vslot, mt + 1);
+          oacc[mt] = mfma_f8(av, PH[nxt], oacc[mt]);
+          vop_hold = av;
+        } else {
+          oacc[mt] = mfma_f8(vop_hold, PL[nxt], oacc[mt]);
+        }
+      } else {
+        lacc = mfma_f8(ones, i == 2 * NMT ? PH[nxt] : PL[nxt], lacc);
+      }
+      if (i < 8) exp_unit(i, c0, c1, PH[cur], PL[cur], nb);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    lexact = lexact * alpha + (pe[0] + pe[1]);
+    pin(PH[cur]);
+    pin(PL[cur]);
+    pin(lexact);
+    step_barrier<2 * NV_STEP>();
+    rescale(alpha);
+  };
+
+  int j = 0;
+  edge_step(j++);
+  for (; j + 4 < jend_w; j += 4) {
+    steady_step(Int<0>(), j);
+    steady_step(Int<1>(), j + 1);
+    steady_step(Int<2>(), j + 2);
+    steady_step(Int<3>(), j + 3);
   }
+  for (; j <= jend; ++j) edge_step(j);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // ---- epilogue: O / l (l: the sum of hi + lo, so the 2^8 cancels), and
