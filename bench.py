@@ -23,13 +23,18 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_TFLOPS = {"bf16": 2516.6, "fp8": 5033.2, "f32": 157.3}   # MI355X dense MFMA
+PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "fp8": 5033.2, "f32": 157.3}   # MI355X dense MFMA
+# whole-chip v_exp_f32 rate at the published clock: 256 CUs x 4 SIMDs x 8 lanes
+# per clock (a wave64 v_exp_f32 takes 8 clocks of issue, measured) x 2.4 GHz
+EXP_PER_S = 256 * 4 * 8 * 2.4e9
 HBM_GBPS = 8000.0
 # sources of each dtype's kernel: a committed traffic summary is used only
 # while these are unchanged
 KERNEL_SOURCES = {
     "bf16": ["tensorized_online_softmax_amd/csrc/attn_fwd_kernels.hpp",
              "tensorized_online_softmax_amd/csrc/softmax_tile.hpp"],
+    "f16": ["tensorized_online_softmax_amd/csrc/attn_fwd_kernels.hpp",
+            "tensorized_online_softmax_amd/csrc/softmax_tile.hpp"],
     "f32": ["tensorized_online_softmax_amd/csrc/attn_fwd_kernels.hpp",
             "tensorized_online_softmax_amd/csrc/softmax_tile.hpp"],
     "fp8": ["tensorized_online_softmax_amd/csrc/attn_fwd_kernels.hpp",
@@ -66,6 +71,16 @@ def read_traffic(workload, dtype):
         return None
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, inp, target_rows):
     """The fp64 oracle (exact attention) on a seeded sample of the workload's
     rows, on every host core this process may use."""
@@ -91,7 +106,8 @@ def cpu_baseline(w, inp, target_rows):
     what = ("every query row" if target_rows == BH * w.N
             else f"{target_rows} of {BH * w.N} query rows (seeded uniform)")
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(), "seconds": round(dt, 3),
+            "gflops_fp64": round(flops / dt / 1e9, 3),
             "sample": f"{what} of the workload, each over its full key range; fp64 exact "
                       f"attention (oracle_attn_exact), {dt:.1f} s"}
 
@@ -124,6 +140,54 @@ def mfma_ceiling():
     print(json.dumps(out), flush=True)
 
 
+def grid_sweep(dtypes, steps, warmup):
+    """The page's workload grid: per point, the kernel at X = 32 (the surrogate
+    tile) and at X = 1 (the per-row online softmax, the FlashAttention-2 analog),
+    both with the vector-unit row sum.  The two settings alternate launch by
+    launch, so that clock and power drift falls on both alike; each reports
+    the median of its launches."""
+    import torch
+    from tensorized_online_softmax_amd import binding, inputs
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    for w in inputs.grid(tuple(dtypes)):
+        inp = inputs.make_workload(w)
+        q, k, v = (inp[n].cuda() for n in ("q", "k", "v"))
+        odt = {"f32": torch.float32, "f16": torch.float16}.get(w.dtype, torch.bfloat16)
+        o = torch.empty((w.B, w.H, w.N, w.d), dtype=odt, device="cuda")
+        lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
+        descale = inp["descale"] if w.dtype == "fp8" else None
+
+        def step(x):
+            binding.attn_fwd(q, k, v, causal=w.causal, scale=w.scale, dtype=w.dtype,
+                             x_tile=x, descale=descale, out=o, lse=lse)
+        xs = (32, 1)
+        for _ in range(warmup):
+            for x in xs:
+                step(x)
+        ev = {x: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(steps)] for x in xs}
+        torch.cuda.synchronize()
+        for i in range(steps):
+            for x in xs:
+                ev[x][i][0].record(stream)
+                step(x)
+                ev[x][i][1].record(stream)
+        torch.cuda.synchronize()
+        line = {"workload": w.name, "dtype": w.dtype, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                "causal": w.causal, "flops": w.flops(), "launches": steps}
+        for x in xs:
+            t = sorted(a.elapsed_time(b) / 1e3 for a, b in ev[x])
+            med = t[len(t) // 2]
+            tf = w.flops() / med / 1e12
+            line[f"x{x}_us"] = round(med * 1e6, 2)
+            line[f"x{x}_tflops"] = round(tf, 1)
+            line[f"x{x}_frac"] = round(tf / PEAK_TFLOPS[w.dtype], 4)
+        line["speedup_x32_over_x1"] = round(line["x1_us"] / line["x32_us"], 4)
+        print(json.dumps(line), flush=True)
+        del q, k, v, o, lse, inp
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -137,6 +201,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=0, help="0 = every row")
     ap.add_argument("--copy-calib-mib", type=int, default=0)
+    ap.add_argument("--grid", default=None, metavar="DTYPES",
+                    help="instead of the attention bench: time every point of the page's "
+                         "workload grid (16k tokens, hidden 2048) for the comma-separated "
+                         "dtypes (bf16,f16,fp8), at X = 32 and X = 1; one JSON line per point")
     ap.add_argument("--mfma-ceiling", action="store_true",
                     help="instead of the attention bench: time torch's bf16 GEMM (the vendor "
                          "library) on random and on all-zero data, for the MFMA throughput this "
@@ -144,6 +212,9 @@ def main():
     args = ap.parse_args()
     if args.mfma_ceiling:
         mfma_ceiling()
+        return
+    if args.grid:
+        grid_sweep(args.grid.split(","), args.steps, args.warmup)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -163,7 +234,7 @@ def main():
     inp = inputs.make_workload(w)
     torch.cuda.set_device(0)
     q, k, v = (inp[n].cuda() for n in ("q", "k", "v"))
-    odt = torch.float32 if w.dtype == "f32" else torch.bfloat16
+    odt = {"f32": torch.float32, "f16": torch.float16}.get(w.dtype, torch.bfloat16)
     o = torch.empty((w.B, w.H, w.N, w.d), dtype=odt, device="cuda")
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
     descale = inp["descale"] if w.dtype == "fp8" else None
@@ -189,6 +260,7 @@ def main():
     wall = time.perf_counter() - t0
     launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     avg_launch_s = sum(launch_ms) / len(launch_ms) / 1e3
+    med_launch_s = sorted(launch_ms)[len(launch_ms) // 2] / 1e3
     ms_per_step = wall * 1e3 / args.steps
     flops = w.flops()
     print(f"[bench] {args.steps} steps in {wall:.3f} s; launch avg {avg_launch_s * 1e6:.1f} us "
@@ -208,7 +280,13 @@ def main():
     peak = PEAK_TFLOPS[w.dtype]
     achieved = flops / avg_launch_s / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(achieved / peak, 4), "traffic": read_traffic(w.name, w.dtype)}
+                "frac": round(achieved / peak, 4), "traffic": read_traffic(w.name, w.dtype),
+                # the secondary (vector) ceiling: one v_exp_f32 per attention element
+                "exp_per_launch": w.exps(), "exp_floor_us": round(w.exps() / EXP_PER_S * 1e6, 2),
+                "launch_us": {"mean": round(avg_launch_s * 1e6, 2),
+                              "median": round(med_launch_s * 1e6, 2),
+                              "min": round(min(launch_ms) * 1e3, 2)},
+                "achieved_at_median": round(flops / med_launch_s / 1e12, 2)}
     result = {
         "metric": "fused attention fwd TFLOP/s at 1 GPU and % of MFMA peak (bf16, fp8)",
         "value": round(flops / (ms_per_step / 1e3) / 1e12, 2),

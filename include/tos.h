@@ -53,9 +53,11 @@ typedef enum {
 typedef enum {
     TOS_F32 = 0,       /* q, k, v, o: float32                                       */
     TOS_BF16 = 1,      /* q, k, v, o: bfloat16                                      */
-    TOS_FP8_E4M3 = 2   /* q, k, v: OCP float8 e4m3fn codes (x = descale * code);
+    TOS_FP8_E4M3 = 2,  /* q, k, v: OCP float8 e4m3fn codes (x = descale * code);
                           o: bfloat16; descales are required in the options;
                           d = 128 only (other head dims: TOS_ERR_UNSUPPORTED)     */
+    TOS_F16 = 3        /* q, k, v, o: IEEE float16 (the same kernel family as
+                          bf16, with the fp16 matrix instructions)                */
 } tos_dtype;
 
 /* How the softmax row sum l is computed (FlashAttention-T section A2,
@@ -64,7 +66,7 @@ typedef enum {
     TOS_SPLIT_VALU = 0,         /* vector-unit dot products of the packed P~ pairs
                                    with (1, 1)                                      */
     TOS_SPLIT_ROWSUM_MFMA = 1   /* matrix-unit contraction of the packed P~ against a
-                                   constant all-ones operand (bf16; not fp32)       */
+                                   constant all-ones operand (bf16, f16; not fp32)  */
 } tos_softmax_split;
 /* Either way l sums the rounded P~ that the P~V product consumes, and a separate
  * unrounded fp32 sum gives lse.  TOS_FP8_E4M3 has no vector form for e4m3
@@ -88,7 +90,7 @@ typedef struct {
     int softmax_split;     /* a tos_softmax_split value                             */
     int fallback;          /* a tos_fallback value                                  */
     float fallback_tau;    /* AUTO threshold in log2 units; 0 = default (100 for
-                              f32/bf16 P~, 12 for e4m3 P~)                          */
+                              f32/bf16 P~, 24 for f16 P~, 12 for e4m3 P~)           */
     float q_descale;       /* fp8 only: real value = descale * stored code; > 0    */
     float k_descale;
     float v_descale;
@@ -103,8 +105,8 @@ typedef struct {
  *   q, k, v   device pointers, [B][H][N][d] of `dtype` (see tos_dtype); the
  *             values must be finite (NaN or infinite inputs give unspecified
  *             outputs)
- *   o         device pointer, [B][H][N][d]: float32 for TOS_F32, bfloat16
- *             otherwise; must not overlap q, k, v or lse
+ *   o         device pointer, [B][H][N][d]: float32 for TOS_F32, float16 for
+ *             TOS_F16, bfloat16 otherwise; must not overlap q, k, v or lse
  *   lse       device pointer to [B][H][N] float32 natural-log log-sum-exp of the
  *             scaled logits, or NULL to skip it
  *   B, H, N   batch, heads, sequence length; >= 0 (any zero: nothing to do,

@@ -8,5 +8,5 @@ arithmetic lives there, in plain loops that follow the FlashAttention-T page
 (sections A2 and A3, Fig 2(a), Algorithm 1).
 """
 from .oracle import (Oracle, attn_exact, attn_surrogate, round_bf16, round_e4m3,  # noqa: F401
-                     max_threads, FALLBACK_OFF, FALLBACK_AUTO, FALLBACK_FORCE,
-                     P_EXACT, P_BF16, P_E4M3)
+                     round_f16, max_threads, FALLBACK_OFF, FALLBACK_AUTO, FALLBACK_FORCE,
+                     P_EXACT, P_BF16, P_E4M3, P_F16)

@@ -119,12 +119,31 @@ double oracle_round_e4m3(double x)
     return x < 0 ? -r : r;
 }
 
-/* p_round: 0 = exact (fp64), 1 = bf16, 2 = e4m3 after multiplying by 2^p_shift */
+/* IEEE binary16: 11 significant bits, min normal 2^-14, subnormal spacing
+ * 2^-24, largest finite 65504; values that round past it become infinite. */
+double oracle_round_f16(double x)
+{
+    if (x == 0.0 || !isfinite(x)) return x;
+    double ax = fabs(x), r;
+    if (ax < ldexp(1.0, -14)) {
+        r = ldexp(nearbyint(ldexp(ax, 24)), -24);
+    } else {
+        int e;
+        double f = frexp(ax, &e);
+        r = ldexp(nearbyint(ldexp(f, 11)), e - 11);
+        if (r > 65504.0) r = INFINITY;
+    }
+    return x < 0 ? -r : r;
+}
+
+/* p_round: 0 = exact (fp64), 1 = bf16, 2 = e4m3, 3 = fp16, after multiplying
+ * by 2^p_shift */
 static double round_p(double p, int p_round, int p_shift)
 {
     switch (p_round) {
     case 1: return oracle_round_bf16(ldexp(p, p_shift));
     case 2: return oracle_round_e4m3(ldexp(p, p_shift));
+    case 3: return oracle_round_f16(ldexp(p, p_shift));
     default: return ldexp(p, p_shift);
     }
 }
@@ -233,7 +252,7 @@ int oracle_attn_exact(const double* q, const double* k, const double* v,
 /*   Bc       keys per block (>= 1)                                           */
 /*   order    NULL or a permutation of 0..ceil(N/Bc)-1: block visiting order  */
 /*   fallback 0 OFF, 1 AUTO (threshold tau, in log2 units), 2 FORCE          */
-/*   p_round  0 exact, 1 bf16, 2 e4m3 -- rounding of P~ (after x 2^p_shift)    */
+/*   p_round  0 exact, 1 bf16, 2 e4m3, 3 fp16 -- rounding of P~ (x 2^p_shift)  */
 /* Outputs (any may be NULL except o and lse)                                  */
 /*   o [BH][N][d], lse [BH][N]                                                */
 /*   ref_out [BH][N]  final reference max of each row (raw dot-product units) */
@@ -255,7 +274,7 @@ int oracle_attn_surrogate(const double* q, const double* k, const double* v,
 {
     if (BH < 0 || N < 0 || d < 1 || X < 1 || Bc < 1) return -1;
     if (!(scale > 0.0) || !isfinite(scale)) return -1;
-    if (fallback < 0 || fallback > 2 || p_round < 0 || p_round > 2) return -1;
+    if (fallback < 0 || fallback > 2 || p_round < 0 || p_round > 3) return -1;
     const int64_t nblk = (N + Bc - 1) / Bc;
     const int64_t ntile = (N + X - 1) / X;
     if (order) {

@@ -11,7 +11,7 @@ import numpy as np
 from . import build as _build
 
 FALLBACK_OFF, FALLBACK_AUTO, FALLBACK_FORCE = 0, 1, 2
-P_EXACT, P_BF16, P_E4M3 = 0, 1, 2
+P_EXACT, P_BF16, P_E4M3, P_F16 = 0, 1, 2, 3
 
 _default = None
 
@@ -36,6 +36,8 @@ def _bind(path):
     lib.oracle_round_bf16.restype = ctypes.c_double
     lib.oracle_round_e4m3.argtypes = [ctypes.c_double]
     lib.oracle_round_e4m3.restype = ctypes.c_double
+    lib.oracle_round_f16.argtypes = [ctypes.c_double]
+    lib.oracle_round_f16.restype = ctypes.c_double
     lib.oracle_max_threads.restype = ctypes.c_int
     lib.oracle_abi_version.restype = ctypes.c_int
     return lib
@@ -67,6 +69,9 @@ class Oracle:
 
     def round_e4m3(self, x):
         return round_e4m3(x, _lib=self._lib)
+
+    def round_f16(self, x):
+        return round_f16(x, _lib=self._lib)
 
 
 def _ptr(a, ctype=ctypes.c_double):
@@ -156,4 +161,9 @@ def round_bf16(x, _lib=None):
 
 def round_e4m3(x, _lib=None):
     f = (_lib or _load()).oracle_round_e4m3
+    return np.vectorize(lambda t: f(float(t)), otypes=[np.float64])(x)
+
+
+def round_f16(x, _lib=None):
+    f = (_lib or _load()).oracle_round_f16
     return np.vectorize(lambda t: f(float(t)), otypes=[np.float64])(x)

@@ -12,7 +12,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libtos.so")
 
 TOS_OK, TOS_ERR_INVALID_ARG, TOS_ERR_UNSUPPORTED, TOS_ERR_HIP = 0, 1, 2, 3
-TOS_F32, TOS_BF16, TOS_FP8_E4M3 = 0, 1, 2
+TOS_F32, TOS_BF16, TOS_FP8_E4M3, TOS_F16 = 0, 1, 2, 3
 TOS_SPLIT_VALU, TOS_SPLIT_ROWSUM_MFMA = 0, 1
 TOS_FALLBACK_OFF, TOS_FALLBACK_AUTO, TOS_FALLBACK_FORCE = 0, 1, 2
 
@@ -109,7 +109,7 @@ def tos_version():
     return int(lib().tos_version())
 
 
-_DTYPE_CODES = {"f32": TOS_F32, "bf16": TOS_BF16, "fp8": TOS_FP8_E4M3}
+_DTYPE_CODES = {"f32": TOS_F32, "bf16": TOS_BF16, "fp8": TOS_FP8_E4M3, "f16": TOS_F16}
 _SPLITS = {"valu": TOS_SPLIT_VALU, "rowsum_mfma": TOS_SPLIT_ROWSUM_MFMA}
 _FALLBACKS = {"off": TOS_FALLBACK_OFF, "auto": TOS_FALLBACK_AUTO, "force": TOS_FALLBACK_FORCE}
 
@@ -132,8 +132,8 @@ def attn_fwd(q, k, v, causal=False, scale=None, dtype=None, x_tile=32, split="va
              out=None, lse=None, stream=None):
     """Allocate O (and lse) with torch and run tos_attn_fwd on the current stream.
 
-    q, k, v: contiguous CUDA tensors [B, H, N, d] of float32, bfloat16 or
-    float8_e4m3fn (then `descale` = {"q":..., "k":..., "v":...} is required).
+    q, k, v: contiguous CUDA tensors [B, H, N, d] of float32, bfloat16, float16
+    or float8_e4m3fn (then `descale` = {"q":..., "k":..., "v":...} is required).
     Returns (o, lse); lse is None when with_lse is False.
     """
     import torch
@@ -141,11 +141,11 @@ def attn_fwd(q, k, v, causal=False, scale=None, dtype=None, x_tile=32, split="va
         raise ValueError("q, k, v must all be [B, H, N, d]")
     B, H, N, d = q.shape
     if dtype is None:
-        dtype = {torch.float32: "f32", torch.bfloat16: "bf16",
+        dtype = {torch.float32: "f32", torch.bfloat16: "bf16", torch.float16: "f16",
                  torch.float8_e4m3fn: "fp8"}[q.dtype]
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    odt = torch.float32 if dtype == "f32" else torch.bfloat16
+    odt = {"f32": torch.float32, "f16": torch.float16}.get(dtype, torch.bfloat16)
     o = out if out is not None else torch.empty((B, H, N, d), dtype=odt, device=q.device)
     if with_lse and lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)

@@ -36,6 +36,40 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
+// 16-bit element types of the second kernel family: bf16 and fp16 share the
+// 32x32x16 MFMA shape, the transposing 16-bit LDS read and every layout; only
+// the MFMA, the dot product with (1, 1) and the conversions differ.
+template <typename E> struct Elem16;
+template <> struct Elem16<__bf16> {
+  // P~ <= 1 is packed as is: bf16 keeps float32's exponent range
+  static constexpr int kPreLog2 = 0;
+  typedef __bf16 v8 __attribute__((ext_vector_type(8)));
+  typedef __bf16 v4 __attribute__((ext_vector_type(4)));
+  typedef __bf16 v2 __attribute__((ext_vector_type(2)));
+  static __device__ __forceinline__ f32x16 mfma(v8 a, v8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ float dot2(v2 a, v2 b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(a, b, c, false);
+  }
+};
+template <> struct Elem16<_Float16> {
+  // fp16 has normals only down to 2^-14: P~ is packed as P~ * 2^15 (at most
+  // 2^15 < 65504, since the reference is at least the row's maximum), so that a
+  // row 29 log2-units below its tile's surrogate still packs normal numbers.
+  // The factor cancels in O / l and is taken out of lse.
+  static constexpr int kPreLog2 = 15;
+  typedef _Float16 v8 __attribute__((ext_vector_type(8)));
+  typedef _Float16 v4 __attribute__((ext_vector_type(4)));
+  typedef _Float16 v2 __attribute__((ext_vector_type(2)));
+  static __device__ __forceinline__ f32x16 mfma(v8 a, v8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ float dot2(v2 a, v2 b, float c) {
+    return __builtin_amdgcn_fdot2(a, b, c, false);
+  }
+};
+
 struct FwdArgs {
   const void* q;
   const void* k;
@@ -81,7 +115,8 @@ __device__ __forceinline__ void count_tiles(const FwdArgs& a, const RowState& st
 }
 
 // ---------------------------------------------------------------------------
-// bf16: v_mfma_f32_32x32x16_bf16 for both products, software-pipelined.
+// 16-bit inputs (bf16, fp16): v_mfma_f32_32x32x16_{bf16,f16} for both
+// products, software-pipelined.  (Below, "bf16" stands for either.)
 //
 // A workgroup has 8 waves = 256 query rows (waves w and w+4 share a SIMD) and
 // one LDS ring of key blocks.  Each wave runs its own three-stage pipeline: in
@@ -199,8 +234,11 @@ template <typename T> __device__ __forceinline__ void pin(const T& x) {
 template <int I> struct Int { static constexpr int value = I; };
 
 
-template <int D, bool CAUSAL, int X, bool ROWSUM_MFMA, bool FB_AUTO>
-__global__ __launch_bounds__(kPThreads, 1) void attn_fwd_bf16(FwdArgs a) {
+template <typename E, int D, bool CAUSAL, int X, bool ROWSUM_MFMA, bool FB_AUTO>
+__global__ __launch_bounds__(kPThreads, 1) void attn_fwd_h16(FwdArgs a) {
+  typedef typename Elem16<E>::v8 ev8;
+  typedef typename Elem16<E>::v4 ev4;
+  typedef typename Elem16<E>::v2 ev2;
   static_assert(D == 64 || D == 128, "head dim");
   constexpr int RB = 2 * D;                   // bytes per K or V row
   constexpr int BLK = kBc * RB;               // bytes per key block of K or V
@@ -225,9 +263,9 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_bf16(FwdArgs a) {
   const int qrow = q0 + 32 * w + ln;
   const bool qvalid = qrow < N;
   const size_t head = (size_t)bh * N * D;
-  const __bf16* Q = (const __bf16*)a.q + head;
-  const u32x4 kdesc = buffer_desc((const __bf16*)a.k + head, (unsigned)N * RB);
-  const u32x4 vdesc = buffer_desc((const __bf16*)a.v + head, (unsigned)N * RB);
+  const E* Q = (const E*)a.q + head;
+  const u32x4 kdesc = buffer_desc((const E*)a.k + head, (unsigned)N * RB);
+  const u32x4 vdesc = buffer_desc((const E*)a.v + head, (unsigned)N * RB);
 
   // key blocks: all of them, or (causal) up to the workgroup's last query
   const int nblk = (N + kBc - 1) / kBc;
@@ -239,13 +277,13 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_bf16(FwdArgs a) {
   const int klim = qvalid ? (CAUSAL ? qrow + 1 : N) : 0;   // keys this lane may see
 
   // Q^T operand: lane (query ln, half hf) holds Q[qrow][16 kk + 8 hf + 0..7]
-  bf16x8 qf[NKK];
+  ev8 qf[NKK];
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk) {
     if (qvalid)
-      qf[kk] = *(const bf16x8*)(Q + (size_t)qrow * D + 16 * kk + 8 * hf);
+      qf[kk] = *(const ev8*)(Q + (size_t)qrow * D + 16 * kk + 8 * hf);
     else
-      qf[kk] = bf16x8{};
+      qf[kk] = ev8{};
   }
 
   // direct-to-LDS loads: instruction k of this wave fills LDS bytes
@@ -292,44 +330,44 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_bf16(FwdArgs a) {
   float lsum = 0.0f;    // row sum of the rounded P~ (VALU; this lane's keys only)
   f32x16 lacc = {};     // the same on the MFMA (every register holds the full sum)
   float lexact = 0.0f;  // row sum of the unrounded P~ (this lane's keys only)
-  bf16x8 ones;
+  ev8 ones;
 #pragma unroll
-  for (int t = 0; t < 8; ++t) ones[t] = (__bf16)1.0f;
-  const bf16x2 ones2 = {(__bf16)1.0f, (__bf16)1.0f};
+  for (int t = 0; t < 8; ++t) ones[t] = (E)1.0f;
+  const ev2 ones2 = {(E)1.0f, (E)1.0f};
 
   // ---- operands and single matrix instructions
   // QK instruction g (0 <= g < NQK) of S^T = K Q^T: key tile t = g % 2,
   // k-step kk = g / 2; its K operand comes from the K block at kt
   constexpr int NQK = 2 * NKK, NPV = 4 * NMT;
-  auto kread = [&](const char* kt, int g) -> bf16x8 {
-    return *(const bf16x8*)(kt + koff[g / 2] + (g % 2) * 32 * RB);
+  auto kread = [&](const char* kt, int g) -> ev8 {
+    return *(const ev8*)(kt + koff[g / 2] + (g % 2) * 32 * RB);
   };
-  auto qk_mfma = [&](int g, bf16x8 av, f32x16& t0, f32x16& t1) {
+  auto qk_mfma = [&](int g, ev8 av, f32x16& t0, f32x16& t1) {
     f32x16& acc = (g % 2) ? t1 : t0;
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[g / 2], g < 2 ? f32x16{} : acc, 0, 0, 0);
+    acc = Elem16<E>::mfma(av, qf[g / 2], g < 2 ? f32x16{} : acc);
   };
   // PV instruction i (0 <= i < NPV) of O^T += V^T P~^T: 16-key step s = i / NMT,
   // M tile mt = i % NMT.  Step s, slot t of lane half h is key
   // 16s + 8(t/4) + 4h + t%4 (the accumulator order of S^T), which the
   // transposing reads fetch.
-  auto vread = [&](const char* vt, int i) -> bf16x8 {
+  auto vread = [&](const char* vt, int i) -> ev8 {
     const char* p = vt + voff[i % NMT] + 16 * (i / NMT) * RB;
     const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p));
     const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p + 8 * RB));
-    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    return __builtin_bit_cast(ev8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
-  auto pv_mfma = [&](int i, bf16x8 av, const bf16x8* pk) {
-    oacc[i % NMT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pk[i / NMT], oacc[i % NMT], 0, 0, 0);
+  auto pv_mfma = [&](int i, ev8 av, const ev8* pk) {
+    oacc[i % NMT] = Elem16<E>::mfma(av, pk[i / NMT], oacc[i % NMT]);
     if constexpr (ROWSUM_MFMA)   // step 7 on the matrix unit: ones x P~^T
       if (i % NMT == NMT - 1)
-        lacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pk[i / NMT], lacc, 0, 0, 0);
+        lacc = Elem16<E>::mfma(ones, pk[i / NMT], lacc);
   };
   auto qk = [&](int slot, f32x16& t0, f32x16& t1) {
     const char* kt = smem + slot * BLK;
 #pragma unroll
     for (int g = 0; g < NQK; ++g) qk_mfma(g, kread(kt, g), t0, t1);
   };
-  auto pv = [&](int slot, const bf16x8* pk) {
+  auto pv = [&](int slot, const ev8* pk) {
     const char* vt = vring + slot * BLK;
 #pragma unroll
     for (int i = 0; i < NPV; ++i) pv_mfma(i, vread(vt, i), pk);
@@ -371,29 +409,29 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_bf16(FwdArgs a) {
   auto tile_ref = [&]() { ref_new = block_ref<X, FB_AUTO>(st, c, tau); };
   auto advance = [&](float& alpha, float& nb) {
     alpha = ref_advance(st, ref_new, c);
-    nb = neg_c_ref(st, c);
+    nb = neg_c_ref(st, c) + (float)Elem16<E>::kPreLog2;
   };
   // steps 4-7 for registers r, r+1 of tile t (unit k: t = k / 8,
-  // r = 2 (k % 8)): P~ = exp2(c*S - c*ref), packed to bf16 as the B operand
+  // r = 2 (k % 8)): P~ = exp2(c*S - c*ref), packed to 16 bits as the B operand
   // of the P~V product, and both row sums.  The unrounded sum gives lse; the
   // sum of the rounded P~ that the product consumes normalises O, so O / l
-  // stays a weighted average of V rows (bf16 rounding of P~ then cancels to
+  // stays a weighted average of V rows (16-bit rounding of P~ then cancels to
   // first order instead of adding to the error of O).
   float pe[2], ps[2];
   auto sums_reset = [&]() { pe[0] = pe[1] = ps[0] = ps[1] = 0.0f; };
-  auto exp_unit = [&](int k, const f32x16& s0, const f32x16& s1, bf16x8* pk, float nb) {
+  auto exp_unit = [&](int k, const f32x16& s0, const f32x16& s1, ev8* pk, float nb) {
     const int t = k / 8, r = 2 * (k % 8);
     const f32x16& sv = t ? s1 : s0;
     const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r], c, nb));
     const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r + 1], c, nb));
     pe[t] += p0;
     pe[t] += p1;
-    bf16x2 w;
-    w[0] = (__bf16)p0;
-    w[1] = (__bf16)p1;
+    ev2 w;
+    w[0] = (E)p0;
+    w[1] = (E)p1;
     pk[2 * t + r / 8][r % 8] = w[0];
     pk[2 * t + r / 8][r % 8 + 1] = w[1];
-    if constexpr (!ROWSUM_MFMA) ps[t] = __builtin_amdgcn_fdot2_f32_bf16(w, ones2, ps[t], false);
+    if constexpr (!ROWSUM_MFMA) ps[t] = Elem16<E>::dot2(w, ones2, ps[t]);
   };
   // the block's sums into the running ones (which absorb alpha here; O and the
   // MFMA row sum get alpha at the end of the step)
@@ -430,9 +468,9 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_bf16(FwdArgs a) {
   // end (after P~_{b-1} V_{b-1}, before P~_b V_b); P~_b V_b in step b+1.
   // Entering step j: S_j in S[0], P~_{j-1} in P[1].
   f32x16 S[2][2];
-  bf16x8 P[2][4];
+  ev8 P[2][4];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) P[0][t] = P[1][t] = bf16x8{};
+  for (int t = 0; t < 4; ++t) P[0][t] = P[1][t] = ev8{};
   S[0][0] = S[0][1] = S[1][0] = S[1][1] = f32x16{};
   if (jend_w > 0) qk(0, S[0][0], S[0][1]);
   // step 0 refills K_0's slot: every wave must be done reading it
@@ -501,7 +539,7 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_bf16(FwdArgs a) {
     const char* vt = vring + (u % kRing) * BLK;         // V_{j-1}
     f32x16 &c0 = S[cur][0], &c1 = S[cur][1], &n0 = S[nxt][0], &n1 = S[nxt][1];
     step_loads(j);
-    bf16x8 kop[LA], vop[LA];
+    ev8 kop[LA], vop[LA];
 #pragma unroll
     for (int g = 0; g < LA; ++g) kop[g] = kread(kt, g);
     float alpha = 1.0f, nb = 0.0f;
@@ -509,7 +547,7 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_bf16(FwdArgs a) {
     // phase A: units 0..EA-1 in the chunks after the chain
 #pragma unroll
     for (int g = 0; g < NQK; ++g) {
-      const bf16x8 av = kop[g % LA];
+      const ev8 av = kop[g % LA];
       if (g + LA < NQK) kop[g % LA] = kread(kt, g + LA);
       else vop[(g + LA - NQK) % LA] = vread(vt, g + LA - NQK);
       qk_mfma(g, av, n0, n1);
@@ -522,7 +560,7 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_bf16(FwdArgs a) {
     // phase B: units EA..15 spread over the chunks
 #pragma unroll
     for (int i = 0; i < NPV; ++i) {
-      const bf16x8 av = vop[i % LA];
+      const ev8 av = vop[i % LA];
       if (i + LA < NPV) vop[i % LA] = vread(vt, i + LA);
       pv_mfma(i, av, P[nxt]);
 #pragma unroll
@@ -563,20 +601,21 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_bf16(FwdArgs a) {
   const float le = pair_reduce(lexact, [](float x, float y) { return x + y; });
   const float inv = l > 0.0f ? a.o_scale / l : 0.0f;
   if (qvalid) {
-    __bf16* O = (__bf16*)a.o + head + (size_t)qrow * D;
+    E* O = (E*)a.o + head + (size_t)qrow * D;
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        bf16x4 ov;
+        ev4 ov;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) ov[u] = (__bf16)(oacc[mt][4 * g + u] * inv);
-        *(bf16x4*)(O + 32 * mt + 8 * g + 4 * hf) = ov;
+        for (int u = 0; u < 4; ++u) ov[u] = (E)(oacc[mt][4 * g + u] * inv);
+        *(ev4*)(O + 32 * mt + 8 * g + 4 * hf) = ov;
       }
     }
     if (a.lse != nullptr && hf == 0)
       a.lse[(size_t)bh * N + qrow] =
-          le > 0.0f ? a.lse_scale * st.ref + __logf(le) : -__builtin_inff();
+          le > 0.0f ? a.lse_scale * st.ref + (__logf(le) - (float)Elem16<E>::kPreLog2 * 0.69314718f)
+                    : -__builtin_inff();
   }
   count_tiles<X, FB_AUTO>(a, st, lane, qrow);
 }

@@ -17,6 +17,7 @@ struct KernelChoice {
 // Each returns hipSuccess, hipErrorNotSupported for a combination that has no
 // instance, or the launch error.
 hipError_t launch_bf16(const FwdArgs& a, const KernelChoice& k, hipStream_t stream);
+hipError_t launch_f16(const FwdArgs& a, const KernelChoice& k, hipStream_t stream);
 hipError_t launch_f32(const FwdArgs& a, const KernelChoice& k, hipStream_t stream);
 hipError_t launch_fp8(const FwdArgs& a, const KernelChoice& k, hipStream_t stream);
 

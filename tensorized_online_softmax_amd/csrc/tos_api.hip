@@ -30,7 +30,7 @@ bool log_enabled() {
   return on;
 }
 
-size_t in_elem_bytes(tos_dtype dt) { return dt == TOS_F32 ? 4 : (dt == TOS_BF16 ? 2 : 1); }
+size_t in_elem_bytes(tos_dtype dt) { return dt == TOS_F32 ? 4 : (dt == TOS_FP8_E4M3 ? 1 : 2); }
 size_t out_elem_bytes(tos_dtype dt) { return dt == TOS_F32 ? 4 : 2; }
 
 }  // namespace
@@ -88,7 +88,8 @@ tos_status tos_attn_fwd(const void* q, const void* k, const void* v, void* o, fl
   if (!std::isfinite(op.fallback_tau) || op.fallback_tau < 0.0f) return TOS_ERR_INVALID_ARG;
 
   // ---- sizes and scalars
-  if (dtype != TOS_F32 && dtype != TOS_BF16 && dtype != TOS_FP8_E4M3) return TOS_ERR_INVALID_ARG;
+  if (dtype != TOS_F32 && dtype != TOS_BF16 && dtype != TOS_FP8_E4M3 && dtype != TOS_F16)
+    return TOS_ERR_INVALID_ARG;
   if (B < 0 || H < 0 || N < 0 || d < 0) return TOS_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return TOS_ERR_INVALID_ARG;
   if (!std::isfinite(scale) || !(scale > 0.0f)) return TOS_ERR_INVALID_ARG;
@@ -145,8 +146,10 @@ tos_status tos_attn_fwd(const void* q, const void* k, const void* v, void* o, fl
   a.c = (float)((double)scale * qk_descale * kLog2e);
   a.o_scale = dtype == TOS_FP8_E4M3 ? op.v_descale : 1.0f;
   // default thresholds: bf16/fp32 P~ keep 2^-100 far above their underflow;
-  // e4m3 P~ (pre-scaled by 2^8) keeps every row's largest term >= 2^-12
-  a.tau = op.fallback_tau > 0.0f ? op.fallback_tau : (dtype == TOS_FP8_E4M3 ? 12.0f : 100.0f);
+  // e4m3 P~ (pre-scaled by 2^8) keeps every row's largest term >= 2^-4; fp16
+  // P~ (pre-scaled by 2^15) keeps it >= 2^-9, a normal number
+  a.tau = op.fallback_tau > 0.0f ? op.fallback_tau
+                                 : (dtype == TOS_FP8_E4M3 ? 12.0f : (dtype == TOS_F16 ? 24.0f : 100.0f));
   a.fallback_tiles = op.fallback_tiles;
   // FORCE runs the per-row kernel and counts every X-row tile of the request
   a.count_x = op.fallback == TOS_FALLBACK_FORCE ? op.x_tile : 0;
@@ -156,6 +159,8 @@ tos_status tos_attn_fwd(const void* q, const void* k, const void* v, void* o, fl
   hipError_t e = hipErrorNotSupported;
   if (dtype == TOS_BF16)
     e = tos::launch_bf16(a, kc, s);
+  else if (dtype == TOS_F16)
+    e = tos::launch_f16(a, kc, s);
   else if (dtype == TOS_F32)
     e = tos::launch_f32(a, kc, s);
   else

@@ -8,7 +8,7 @@ Recipe (shared by every workload):
   * numpy ``default_rng(seed)`` (PCG64) draws float32 N(0, 1) values on the host,
     in [B, H, N, d] order, one generator per tensor (seed + 1 for Q, + 2 for K,
     + 3 for V, + 4 for the spike placement);
-  * bf16 storage: a round-to-nearest-even cast of those float32 values;
+  * bf16 and fp16 storage: a round-to-nearest-even cast of those float32 values;
   * fp8 storage (OCP e4m3fn): per-tensor descale s = amax / 448, values x / s
     clamped to [-448, 448] and cast with round-to-nearest-even; the real value of
     a stored code c is s * c.
@@ -24,7 +24,7 @@ import math
 import numpy as np
 import torch
 
-DTYPES = ("f32", "bf16", "fp8")
+DTYPES = ("f32", "bf16", "f16", "fp8")
 
 
 @dataclass(frozen=True)
@@ -34,7 +34,7 @@ class Workload:
     H: int
     N: int
     d: int
-    dtype: str            # "f32" | "bf16" | "fp8"
+    dtype: str            # "f32" | "bf16" | "f16" | "fp8"
     causal: bool
     x_tile: int           # surrogate tile rows X
     seed: int             # base seed: Q = seed+1, K = seed+2, V = seed+3, spikes = seed+4
@@ -52,6 +52,12 @@ class Workload:
         f = 4.0 * self.B * self.H * self.N * self.N * self.d
         return f / 2 if self.causal else f
 
+    def exps(self) -> float:
+        """Exponentials of the algorithm: one per (query, key) element, halved
+        when causal (the diagonal elements aside)."""
+        e = float(self.B * self.H * self.N * self.N)
+        return e / 2 if self.causal else e
+
 
 WORKLOADS = {
     "single_head_f32": Workload("single_head_f32", 1, 1, 128, 64, "f32", False, 16, 1000,
@@ -62,6 +68,12 @@ WORKLOADS = {
                             note="causal, bf16, d=128, N=4096"),
     "long_causal_bf16": Workload("long_causal_bf16", 1, 16, 16384, 128, "bf16", True, 32, 4000,
                                  note="long-sequence causal, bf16, d=128, N=16384"),
+    # one GPU's share of the causal workload on an 8-GPU node sharded by heads
+    # (no exchange between GPUs): 4 of the 32 heads
+    "causal_bf16_shard8": Workload("causal_bf16_shard8", 2, 4, 4096, 128, "bf16", True, 32, 3000,
+                                   note="causal bf16 N=4096 d=128, one GPU's share of 8 (H=4)"),
+    "causal_f16": Workload("causal_f16", 2, 32, 4096, 128, "f16", True, 32, 3000,
+                           note="causal, fp16, d=128, N=4096"),
     "fp8_spiky": Workload("fp8_spiky", 1, 16, 8192, 128, "fp8", False, 32, 5000,
                           std=math.sqrt(8.0), spike_frac=0.2, spike_logit=40.0, fallback="auto",
                           note="fp8 e4m3 stress: logit std 8, 20% of rows with one +40 key"),
@@ -106,6 +118,37 @@ def to_fp8(x: np.ndarray):
     return torch.from_numpy(y).to(torch.float8_e4m3fn), float(np.float32(s))
 
 
+# The FlashAttention-T page's benchmark grid (section A4, "experimental
+# setup"): 16k tokens in total and a hidden size of 2048 at every sequence
+# length, so B = 16384 / N and H = 2048 / d.
+GRID_TOKENS = 16384
+GRID_HIDDEN = 2048
+GRID_N = (512, 1024, 2048, 4096, 8192)
+GRID_D = (64, 128)
+
+
+def grid_workload(N, d, dtype, causal, x_tile=32, seed=6000):
+    """One point of the page's grid as a Workload (named grid_<dtype>_<c|nc>_N<N>_d<d>)."""
+    if GRID_TOKENS % N or GRID_HIDDEN % d:
+        raise ValueError("N must divide 16384 and d must divide 2048")
+    name = f"grid_{dtype}_{'c' if causal else 'nc'}_N{N}_d{d}"
+    return Workload(name, GRID_TOKENS // N, GRID_HIDDEN // d, N, d, dtype, bool(causal), x_tile,
+                    seed + N + d, note="16k tokens, hidden 2048")
+
+
+def grid(dtypes=("bf16", "f16", "fp8"), causal=(False, True)):
+    """Every point of the page's grid that the library supports (fp8: d = 128)."""
+    out = []
+    for dt in dtypes:
+        for c in causal:
+            for d in GRID_D:
+                if dt == "fp8" and d != 128:
+                    continue
+                for n in GRID_N:
+                    out.append(grid_workload(n, d, dt, c))
+    return out
+
+
 def make(B, H, N, d, dtype, seed, std=1.0, spike_frac=0.0, spike_logit=0.0, scale=None):
     """Draw Q, K, V for one problem.
 
@@ -124,8 +167,9 @@ def make(B, H, N, d, dtype, seed, std=1.0, spike_frac=0.0, spike_logit=0.0, scal
     descale = {"q": 1.0, "k": 1.0, "v": 1.0}
     if dtype == "f32":
         tq, tk, tv = (torch.from_numpy(np.ascontiguousarray(a)) for a in (q, k, v))
-    elif dtype == "bf16":
-        tq, tk, tv = (torch.from_numpy(np.ascontiguousarray(a)).to(torch.bfloat16) for a in (q, k, v))
+    elif dtype in ("bf16", "f16"):
+        tdt = torch.bfloat16 if dtype == "bf16" else torch.float16
+        tq, tk, tv = (torch.from_numpy(np.ascontiguousarray(a)).to(tdt) for a in (q, k, v))
     else:
         (tq, sq), (tk, sk), (tv, sv) = to_fp8(q), to_fp8(k), to_fp8(v)
         descale = {"q": sq, "k": sk, "v": sv}

@@ -302,6 +302,36 @@ def pin_fallback(orc):
         assert np.abs(rb["o"] - o_ref).max() <= 1e-2
 
 
+def pin_fallback_f16(orc):
+    """fp16 P~ (x 2^15, normals down to 2^-14) flushes the flat rows of a tile that
+    holds a spiked row (a gap of about 58 log2 units) without the fallback; AUTO
+    at the fp16 default tau = 24 switches those tiles and recovers exact
+    attention to fp16 precision, and N(0,1) inputs never switch."""
+    rng = np.random.default_rng(16)
+    BH, N, d = 2, 256, 64
+    scale = 1.0 / math.sqrt(d)
+    q, k, v = _spiky(rng, BH, N, d, 8.0, 0.2, 40.0, scale)
+    o_ref, lse_ref = orc.attn_exact(q, k, v, False, scale)
+    off = orc.attn_surrogate(q, k, v, False, scale, X=32, Bc=64, p_round=3, p_shift=15)
+    flushed = np.isneginf(off["lse"])
+    assert flushed.any(), "no row flushed without the fallback"
+    assert np.all(off["o"][flushed] == 0.0), "flushed rows must give O = 0"
+    r = orc.attn_surrogate(q, k, v, False, scale, X=32, Bc=64, fallback=1, tau=24.0,
+                           p_round=3, p_shift=15)
+    assert r["switched"].sum() > 0 and not np.isneginf(r["lse"]).any()
+    # 11 significant bits: each P~ within 2^-11 relative, O a convex combination
+    # of V rows with |v| < 8 moves by at most about 8 * 2^-11
+    assert np.abs(r["o"] - o_ref).max() <= 8 * 2.0 ** -11
+    assert np.abs(r["lse"] - lse_ref).max() <= math.log1p(2.0 ** -11)
+    q, k, v = (rng.standard_normal((BH, N, d)) for _ in range(3))
+    for causal in (False, True):
+        r = orc.attn_surrogate(q, k, v, causal, scale, X=32, Bc=64, fallback=1, tau=24.0,
+                               p_round=3, p_shift=15)
+        o_ref, lse_ref = orc.attn_exact(q, k, v, causal, scale)
+        assert r["switched"].sum() == 0, "switched on N(0,1) inputs"
+        assert np.abs(r["o"] - o_ref).max() <= 8 * 2.0 ** -11
+
+
 def pin_rounding(orc):
     """Round-to-nearest-even models agree with torch's casts on float32 inputs."""
     rng = np.random.default_rng(17)
@@ -325,8 +355,17 @@ def pin_rounding(orc):
     codes = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
     codes = codes[np.isfinite(codes)]
     assert np.array_equal(orc.round_e4m3(codes), codes), "e4m3 codes are not fixed points"
+    z = np.concatenate([
+        (rng.standard_normal(4000) * 100).astype(np.float32),
+        (rng.standard_normal(2000) * 1e-6).astype(np.float32),         # fp16 subnormals
+        np.array([1.0 + 2.0 ** -11, 1.0 + 3 * 2.0 ** -11, 2.0 ** -25, 3 * 2.0 ** -25,
+                  65504.0, 65519.0, 65520.0, -65520.0, 2.0 ** -14], dtype=np.float32),  # ties, overflow
+    ])
+    want = torch.from_numpy(z).to(torch.float16).to(torch.float64).numpy()
+    got = orc.round_f16(z.astype(np.float64))
+    assert np.array_equal(got, want), "fp16 rounding differs from torch"
 
 
 ALL_PINS = [pin_golden_closed_forms, pin_library_sdpa, pin_special_cases,
             pin_surrogate_equals_exact, pin_surrogate_invariants, pin_per_row_textbook,
-            pin_fallback, pin_rounding]
+            pin_fallback, pin_fallback_f16, pin_rounding]

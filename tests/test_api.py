@@ -94,6 +94,8 @@ def opts(**kw):
     (dict(dtype=tb.TOS_FP8_E4M3, opts=opts(v_descale=float("nan"))), tb.TOS_ERR_INVALID_ARG),
     (dict(dtype=tb.TOS_F32, opts=opts(softmax_split=1)), tb.TOS_ERR_UNSUPPORTED),
     (dict(dtype=tb.TOS_FP8_E4M3, d=64), tb.TOS_ERR_UNSUPPORTED),   # fp8: d = 128 only
+    (dict(dtype=tb.TOS_F16, d=96), tb.TOS_ERR_UNSUPPORTED),
+    (dict(dtype=4), tb.TOS_ERR_INVALID_ARG),
     (dict(B=70000, H=70000), tb.TOS_ERR_UNSUPPORTED),       # grid beyond 2^31
     # empty problems: nothing to do, and no pointer is needed
     (dict(B=0, q=None, k=None, v=None, o=None), tb.TOS_OK),

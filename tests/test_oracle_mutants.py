@@ -39,6 +39,11 @@ MUTANTS = [
     ("lse_shift_sign", "- p_shift * 0.69314718055994530941723212145818", "+ p_shift * 0.69314718055994530941723212145818"),
     ("bf16_one_bit_short", "r = ldexp(nearbyint(ldexp(f, 8)), e - 8);", "r = ldexp(nearbyint(ldexp(f, 7)), e - 7);"),
     ("e4m3_no_subnormals", "r = ldexp(nearbyint(ldexp(ax, 9)), -9);", "r = 0.0;"),
+    ("f16_bf16_precision", "r = ldexp(nearbyint(ldexp(f, 11)), e - 11);",
+     "r = ldexp(nearbyint(ldexp(f, 8)), e - 8);"),
+    ("f16_no_overflow", "if (r > 65504.0) r = INFINITY;", ""),
+    ("f16_model_is_bf16", "case 3: return oracle_round_f16(ldexp(p, p_shift));",
+     "case 3: return oracle_round_bf16(ldexp(p, p_shift));"),
     ("flushed_row_gets_nan", "for (int64_t u = 0; u < d; ++u) oi[u] = 0.0;\n                    lse[row] = -INFINITY;",
      "for (int64_t u = 0; u < d; ++u) oi[u] = O[a * d + u] / l[a];\n                    lse[row] = -INFINITY;"),
 ]

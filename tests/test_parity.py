@@ -27,7 +27,7 @@ def _inp(B, H, N, d, dtype, seed, std=1.0):
 SMALL_N = [1, 17, 64, 100, 130, 257, 383]
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("N", SMALL_N)
@@ -39,14 +39,14 @@ def test_small_full(dtype, d, causal, N):
                  f"{dtype} d={d} causal={causal} N={N}")
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("x_tile", [1, 16, 32])
 @pytest.mark.parametrize("split", ["valu", "rowsum_mfma"])
 @pytest.mark.parametrize("fallback", ["off", "auto", "force"])
 @pytest.mark.parametrize("causal", [False, True])
 def test_knobs(dtype, x_tile, split, fallback, causal):
     if dtype == "f32" and split == "rowsum_mfma":
-        pytest.skip("row sum on the matrix unit is a bf16 option")
+        pytest.skip("row sum on the matrix unit is a 16-bit option")
     inp = _inp(1, 4, 300, 64, dtype, seed=7)
     o_ref, lse_ref = oracle_exact(inp, causal)
     o, lse, tiles = run_gpu(inp, causal, x_tile=x_tile, split=split, fallback=fallback,
@@ -75,6 +75,30 @@ def test_fallback_auto_switches_on_spiky_rows():
             assert tiles > 0
         if fb == "off" or tau == 0.0:
             assert tiles == 0   # default tau (100) is far above these gaps
+
+
+def test_f16_spiky_needs_the_fallback():
+    """fp16 P~ (x 2^15) flushes the flat rows of a tile that holds a spiked row
+    when the fallback is off (their O is then 0); AUTO at the fp16 default tau
+    switches those tiles and matches exact attention."""
+    N, d = 512, 128
+    inp = inputs.make(1, 2, N, d, "f16", seed=56, std=math.sqrt(8.0), spike_frac=0.2,
+                      spike_logit=40.0)
+    o_ref, lse_ref = oracle_exact(inp, False)
+    o, lse, tiles = run_gpu(inp, False, fallback="auto", counter=True)
+    assert tiles > 0
+    assert_close(o.reshape(o_ref.shape), o_ref, lse.reshape(lse_ref.shape), lse_ref, "f16",
+                 "f16 spiky, fallback auto")
+    o_off, _, _ = run_gpu(inp, False, fallback="off")
+    err = np.abs(o_off.reshape(o_ref.shape) - o_ref).max(-1)
+    assert np.all(np.isfinite(o_off)) and err.max() > 0.5
+    # the rows the oracle's fp16 model flushes are the rows that come out 0
+    q, k, v = real_inputs(inp)
+    model = oracle.attn_surrogate(q, k, v, False, inp["scale"], X=32, Bc=64,
+                                  p_round=oracle.P_F16, p_shift=15)
+    flushed = np.isneginf(model["lse"]).reshape(-1)
+    zero = np.all(o_off.reshape(-1, d) == 0.0, axis=-1)
+    assert flushed.any() and np.array_equal(flushed, zero)
 
 
 def test_deterministic():
@@ -165,7 +189,8 @@ def test_fp8_spiky_needs_the_fallback():
 
 
 @pytest.mark.parametrize("name", ["single_head_f32", "mha_bf16", "causal_bf16",
-                                  "long_causal_bf16", "fp8_spiky"])
+                                  "causal_bf16_shard8", "long_causal_bf16", "fp8_spiky",
+                                  "causal_f16"])
 def test_workload_sampled(name):
     w = inputs.WORKLOADS[name]
     inp = inputs.make_workload(w)
@@ -181,3 +206,22 @@ def test_workload_sampled(name):
         rows = sample_rows(BH, w.N, 384, seed=w.seed, causal=w.causal)
         o_ref, lse_ref = oracle_exact(inp, w.causal, rows=rows)
         assert_close(o[rows], o_ref, lse[rows], lse_ref, w.dtype, name)
+
+
+@pytest.mark.parametrize("w", inputs.grid(), ids=lambda w: w.name)
+def test_grid_sampled(w):
+    """The FlashAttention-T page's grid (16k tokens, hidden 2048, N = 512..8192,
+    d = 64 and 128, causal and not, bf16 / fp16 / fp8) in the benchmark's launch
+    configuration, on sampled rows."""
+    inp = inputs.make_workload(w)
+    o, lse, _ = run_gpu(inp, w.causal, x_tile=w.x_tile)
+    BH = w.B * w.H
+    o = o.reshape(BH * w.N, w.d)
+    lse = lse.reshape(BH * w.N)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    rng = np.random.default_rng(w.seed)
+    rows = np.unique(np.concatenate([
+        rng.integers(0, BH * w.N, size=256),
+        [b * w.N + i for b in (0, BH - 1) for i in (0, 1, 63, 64, 255, 256, w.N - 1)]]))
+    o_ref, lse_ref = oracle_exact(inp, w.causal, rows=rows)
+    assert_close(o[rows], o_ref, lse[rows], lse_ref, w.dtype, w.name)
