@@ -102,6 +102,27 @@ __device__ __forceinline__ void block_coords(const FwdArgs& a, bool causal, int&
   q0 = qb * kBr;
 }
 
+// Items of the persistent kernels: item i is query block qb of head bh, with
+// bh = i mod BH and the blocks numbered heaviest first when causal (the query
+// blocks with the most keys).
+__device__ __forceinline__ void item_coords(const FwdArgs& a, bool causal, int i, int& bh, int& qb) {
+  bh = i % a.BH;
+  qb = causal ? (a.nqb - 1 - i / a.BH) : i / a.BH;
+}
+
+// The item that workgroup g of G runs in round r.  Even rounds deal items in
+// order, odd rounds deal them backwards in groups of 8 workgroups, so that a
+// workgroup that got one of the heavier items of a round gets one of the
+// lighter ones of the next (causal work evens out), while workgroup g still
+// gets items of the heads h = g mod 8 (mod 8): with G and BH multiples of 8,
+// the items of a head stay on the XCD that workgroup g runs on (workgroups are
+// dealt to the 8 XCDs round-robin), where its K and V stay in L2.
+// (A G that is not a multiple of 8 deals every round in order.)
+__device__ __forceinline__ int item_of(int r, int g, int G) {
+  const int gg = ((r & 1) && (G & 7) == 0) ? (G - 8 - (g & ~7)) + (g & 7) : g;
+  return r * G + gg;
+}
+
 // Tile counter: once per tile that ran with per-row maxima.
 template <int X, bool FB_AUTO>
 __device__ __forceinline__ void count_tiles(const FwdArgs& a, const RowState& st, int lane,
@@ -177,6 +198,25 @@ __device__ __forceinline__ u32x4 block_desc(u32x4 d, int j, int jlim, unsigned b
   return r;
 }
 
+// c ? x : y for wave-uniform descriptors, as scalar selects (the compiler
+// would otherwise branch around the computation of the one not taken)
+__device__ __forceinline__ u32x4 select_desc(bool c, u32x4 x, u32x4 y) {
+  // (the operands are uniform; readfirstlane says so where the compiler
+  // cannot prove it, and is free where it can)
+  const unsigned cc = __builtin_amdgcn_readfirstlane((unsigned)c);
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    unsigned v;
+    asm("s_cmp_lg_u32 %1, 0\n\ts_cselect_b32 %0, %2, %3"
+        : "=s"(v)
+        : "s"(cc), "s"(__builtin_amdgcn_readfirstlane(x[i])), "s"(__builtin_amdgcn_readfirstlane(y[i]))
+        : "scc");
+    r[i] = v;
+  }
+  return r;
+}
+
 // LDS position (16-byte chunk index within the row) of chunk c of row r
 template <int D> __device__ __forceinline__ int kswz(int r, int c) {
   return D == 128 ? (c ^ (r & 15)) : (c ^ ((r >> 1) & 7));
@@ -248,43 +288,82 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_h16(FwdArgs a) {
   constexpr int NV_STEP = 2 * CHW;            // loads a wave issues per step
   // V ring first: its slot offsets plus the in-block offsets fit the 16-bit
   // immediate of the LDS reads; the K ring's base is folded into koff
-  __shared__ __attribute__((aligned(1024))) char smem[2 * kRing * BLK];
+  // Past the rings, 4 x 32 rows of O staging: each wave transposes its O tile
+  // through LDS (32 rows, waves 0-3 in V slots 2 and 3, free then, waves 4-7
+  // here) so that the stores write whole rows.
+  constexpr int SB = 32 * RB;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kRing * BLK + 4 * SB];
   char* vring = smem;
 
   // the wave index is the same in every lane: say so, so that everything
   // derived from it (block ranges, LDS slots, descriptors) stays scalar
   const int tid = threadIdx.x, lane = tid & 63, ln = lane & 31, hf = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int bid = blockIdx.x;
-  const int bh = bid % a.BH;
-  const int qb = CAUSAL ? (a.nqb - 1 - bid / a.BH) : bid / a.BH;
-  const int q0 = qb * kPBr;
+  // Persistent workgroups: workgroup g of G runs items (query blocks of a
+  // head) item_of(0, g), item_of(1, g), ... until they run out.
   const int N = a.N;
-  const int qrow = q0 + 32 * w + ln;
-  const bool qvalid = qrow < N;
-  const size_t head = (size_t)bh * N * D;
-  const E* Q = (const E*)a.q + head;
-  const u32x4 kdesc = buffer_desc((const E*)a.k + head, (unsigned)N * RB);
-  const u32x4 vdesc = buffer_desc((const E*)a.v + head, (unsigned)N * RB);
-
-  // key blocks: all of them, or (causal) up to the workgroup's last query
   const int nblk = (N + kBc - 1) / kBc;
-  const int qlast_wg = min(q0 + kPBr, N) - 1;
-  const int jend = CAUSAL ? qlast_wg / kBc + 1 : nblk;
-  const int wq0 = q0 + 32 * w;                       // first query of the wave
-  const int wqlast = min(wq0 + 31, N - 1);
-  const int jend_w = (wq0 >= N) ? 0 : (CAUSAL ? wqlast / kBc + 1 : nblk);
-  const int klim = qvalid ? (CAUSAL ? qrow + 1 : N) : 0;   // keys this lane may see
+  const int nitems = a.BH * a.nqb;
+  const int nwg = gridDim.x, gid = blockIdx.x;
+  // key blocks of an item: all of them, or (causal) up to its last query
+  auto item_jend = [&](int q0_) { return CAUSAL ? (min(q0_ + kPBr, N) - 1) / kBc + 1 : nblk; };
+
+  // the current item (wave-uniform, but qrow, qvalid and klim)
+  int bh = 0, q0 = 0, qrow = 0, jend = 0, jend_w = 0, klim = 0;
+  bool qvalid = false;
+  size_t head = 0;
+  u32x4 kdesc = {}, vdesc = {};
+  auto set_item = [&](int it) {
+    int qb;
+    item_coords(a, CAUSAL, it, bh, qb);
+    q0 = qb * kPBr;
+    qrow = q0 + 32 * w + ln;
+    qvalid = qrow < N;
+    head = (size_t)bh * N * D;
+    kdesc = buffer_desc((const E*)a.k + head, (unsigned)N * RB);
+    vdesc = buffer_desc((const E*)a.v + head, (unsigned)N * RB);
+    jend = item_jend(q0);
+    const int wq0 = q0 + 32 * w;                       // first query of the wave
+    jend_w = (wq0 >= N) ? 0 : (CAUSAL ? min(wq0 + 31, N - 1) / kBc + 1 : nblk);
+    klim = qvalid ? (CAUSAL ? qrow + 1 : N) : 0;       // keys this lane may see
+  };
+  // The next item's first K and V blocks are loaded by this item's last steps
+  // (the ring continues across items) when this item's block count is a
+  // multiple of the ring size, so that those blocks land in the slots the
+  // next item expects them in.
+  // Its Q fragments are loaded in this item's last step, after the last use
+  // of this item's.
+  bool pref_next = false;
+  int jend_n = 0, qrow_n = 0;
+  bool qvalid_n = false;
+  size_t head_n = 0;
+  u32x4 kdesc_n = {}, vdesc_n = {};
+  auto set_next = [&](int it) {
+    pref_next = it < nitems && jend % kRing == 0;
+    if (pref_next) {
+      int bh_n, qb_n;
+      item_coords(a, CAUSAL, it, bh_n, qb_n);
+      head_n = (size_t)bh_n * N * D;
+      kdesc_n = buffer_desc((const E*)a.k + head_n, (unsigned)N * RB);
+      vdesc_n = buffer_desc((const E*)a.v + head_n, (unsigned)N * RB);
+      jend_n = item_jend(qb_n * kPBr);
+      qrow_n = qb_n * kPBr + 32 * w + ln;
+      qvalid_n = qrow_n < N;
+    }
+  };
 
   // Q^T operand: lane (query ln, half hf) holds Q[qrow][16 kk + 8 hf + 0..7]
   ev8 qf[NKK];
+  auto load_q = [&](size_t head_, int qrow_, bool qvalid_) {
+    const E* Q = (const E*)a.q + head_;
 #pragma unroll
-  for (int kk = 0; kk < NKK; ++kk) {
-    if (qvalid)
-      qf[kk] = *(const ev8*)(Q + (size_t)qrow * D + 16 * kk + 8 * hf);
-    else
-      qf[kk] = ev8{};
-  }
+    for (int kk = 0; kk < NKK; ++kk) {
+      if (qvalid_)
+        qf[kk] = *(const ev8*)(Q + (size_t)qrow_ * D + 16 * kk + 8 * hf);
+      else
+        qf[kk] = ev8{};
+    }
+  };
 
   // direct-to-LDS loads: instruction k of this wave fills LDS bytes
   // [(w*CHW + k)*1024, +1024) of the slot, lane L the 16 bytes at +16L, i.e.
@@ -299,11 +378,24 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_h16(FwdArgs a) {
   // wave-uniform LDS byte addresses of this wave's share of ring slot 0
   const unsigned lds0 = (unsigned)(unsigned long long)(__attribute__((address_space(3))) char*)smem;
   const unsigned vdst = lds0 + (unsigned)w * CHW * 1024, kdst = vdst + kRing * BLK;
-  auto load_k = [&](int j) {
-    dma_block<CHW>(block_desc(kdesc, j, jend, BLK), kdst + (j % kRing) * BLK, kgoff);
+  // block j of the item's K (V), zeros past its end; with XING (a step that
+  // may cross the item's end) the blocks past the end are the next item's
+  // first ones when those are prefetched
+  auto ring_desc = [&](const u32x4& cur, const u32x4& nxt, int j) -> u32x4 {
+    return select_desc(pref_next & (j >= jend), block_desc(nxt, j - jend, jend_n, BLK),
+                       block_desc(cur, j, jend, BLK));
   };
-  auto load_v = [&](int j) {
-    dma_block<CHW>(block_desc(vdesc, j, jend, BLK), vdst + (j % kRing) * BLK, vgoff);
+  auto load_k = [&](int j, auto XING) {
+    if constexpr (decltype(XING)::value)
+      dma_block<CHW>(ring_desc(kdesc, kdesc_n, j), kdst + (j % kRing) * BLK, kgoff);
+    else
+      dma_block<CHW>(block_desc(kdesc, j, jend, BLK), kdst + (j % kRing) * BLK, kgoff);
+  };
+  auto load_v = [&](int j, auto XING) {
+    if constexpr (decltype(XING)::value)
+      dma_block<CHW>(ring_desc(vdesc, vdesc_n, j), vdst + (j % kRing) * BLK, vgoff);
+    else
+      dma_block<CHW>(block_desc(vdesc, j, jend, BLK), vdst + (j % kRing) * BLK, vgoff);
   };
 
   // K operand reads: lane (key ln of tile t, half hf) reads chunk 2kk + hf of
@@ -322,14 +414,15 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_h16(FwdArgs a) {
     voff[mt] = vr0 * RB + 16 * vswz<D>(vr0, 4 * mt + 2 * (G & 1) + ((gi & 3) >> 1)) + 8 * (gi & 1);
 
   RowState st;
-  row_state_init(st, X == 1);
   const float c = a.c, tau = a.tau;
   f32x16 oacc[NMT];
-#pragma unroll
-  for (int mt = 0; mt < NMT; ++mt) oacc[mt] = f32x16{};
-  float lsum = 0.0f;    // row sum of the rounded P~ (VALU; this lane's keys only)
-  f32x16 lacc = {};     // the same on the MFMA (every register holds the full sum)
-  float lexact = 0.0f;  // row sum of the unrounded P~ (this lane's keys only)
+  float lsum;       // row sum of the rounded P~ (VALU; this lane's keys only)
+  f32x16 lacc;      // the same on the MFMA (every register holds the full sum)
+  float lexact;     // row sum of the unrounded P~ (this lane's keys only)
+  // Pipeline registers: entering step j, S_j in S[0] and P~_{j-1} in P[1]
+  // (the steady steps alternate the two sets)
+  f32x16 S[2][2];
+  ev8 P[2][4];
   ev8 ones;
 #pragma unroll
   for (int t = 0; t < 8; ++t) ones[t] = (E)1.0f;
@@ -448,37 +541,23 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_h16(FwdArgs a) {
       if constexpr (ROWSUM_MFMA) lacc *= alpha;
     }
   };
-  auto step_loads = [&](int j) {
-    load_k(j + kKAhead);
-    load_v(j + kVAhead);
+  auto step_loads = [&](int j, auto XING) {
+    load_k(j + kKAhead, XING);
+    load_v(j + kVAhead, XING);
   };
-
-  // ---- prologue: K_0..K_3 and V_0, V_1 into the rings
-#pragma unroll
-  for (int j = 0; j < kKAhead; ++j) load_k(j);
-#pragma unroll
-  for (int j = 0; j < kVAhead; ++j) load_v(j);
-  step_barrier<0>();
-  // the same wait in a form the compiler sees: the Q fragments (plain global
-  // loads) are complete from here on, so no wait for them lands in the loop
-  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0), expcnt and lgkmcnt untouched
 
   // Pipeline of key block b: S_b = K_b Q^T in step b-1; its tile maximum,
   // exponentials and row sums in step b, where O is rescaled by alpha_b at the
   // end (after P~_{b-1} V_{b-1}, before P~_b V_b); P~_b V_b in step b+1.
-  // Entering step j: S_j in S[0], P~_{j-1} in P[1].
-  f32x16 S[2][2];
-  ev8 P[2][4];
-#pragma unroll
-  for (int t = 0; t < 4; ++t) P[0][t] = P[1][t] = ev8{};
-  S[0][0] = S[0][1] = S[1][0] = S[1][1] = f32x16{};
-  if (jend_w > 0) qk(0, S[0][0], S[0][1]);
-  // step 0 refills K_0's slot: every wave must be done reading it
-  step_barrier<0>();
 
-  // Any step (first, last, idle), slots and masking decided at run time.
+  // Any step (first, last, idle), slots and masking decided at run time.  The
+  // last step (j = jend) loads nothing when the next item is prefetched: its
+  // K slot holds the next item's first block.
   auto edge_step = [&](int j) {
-    step_loads(j);
+    if (pref_next && j == jend)
+      load_q(head_n, qrow_n, qvalid_n);
+    else
+      step_loads(j, Int<1>());
     float alpha = 1.0f, nb = 0.0f;
     if (j < jend_w) {
       if (j == jend_w - 1) mask_block(j, S[0][0], S[0][1]);
@@ -532,13 +611,13 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_h16(FwdArgs a) {
       if (i == 2) advance(alpha, nb);
     }
   };
-  auto steady_step = [&](auto U, int j) {
+  auto steady_step = [&](auto U, int j, auto XING) {
     constexpr int u = decltype(U)::value;
     constexpr int cur = u & 1, nxt = cur ^ 1;
     const char* kt = smem + ((u + 2) % kRing) * BLK;    // K_{j+1}
     const char* vt = vring + (u % kRing) * BLK;         // V_{j-1}
     f32x16 &c0 = S[cur][0], &c1 = S[cur][1], &n0 = S[nxt][0], &n1 = S[nxt][1];
-    step_loads(j);
+    step_loads(j, XING);
     ev8 kop[LA], vop[LA];
 #pragma unroll
     for (int g = 0; g < LA; ++g) kop[g] = kread(kt, g);
@@ -579,45 +658,134 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_h16(FwdArgs a) {
     rescale(alpha);
   };
 
-  int j = 0;
-  edge_step(j++);
-  for (; j + 4 < jend_w; j += 4) {
-    steady_step(Int<0>(), j);
-    steady_step(Int<1>(), j + 1);
-    steady_step(Int<2>(), j + 2);
-    steady_step(Int<3>(), j + 3);
-  }
-  for (; j <= jend; ++j) edge_step(j);
-  // the last steps' loads (zeros past the last block) still write LDS: let
-  // them land before the workgroup can end and its LDS be handed on
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-
-  // ---- epilogue: l, O / l, lse (reading R-7: lse = scale*ref + ln l)
-  float l;
-  if constexpr (ROWSUM_MFMA)
-    l = lacc[0];
-  else
-    l = pair_reduce(lsum, [](float x, float y) { return x + y; });
-  const float le = pair_reduce(lexact, [](float x, float y) { return x + y; });
-  const float inv = l > 0.0f ? a.o_scale / l : 0.0f;
-  if (qvalid) {
-    E* O = (E*)a.o + head + (size_t)qrow * D;
+  // ---- epilogue of an item: l, O / l, lse (reading R-7: lse = scale*ref + ln l).
+  // finish() computes them and puts this wave's O rows (32 x D) in its LDS
+  // staging area, row r's 16-byte chunk c at position c xor (r mod CPR);
+  // flush() stores them, whole rows per instruction, after the next item's
+  // prologue wait, so that the stores do not hold up that wait.
+  constexpr int CPR = RB / 16;                  // 16-byte chunks per row
+  char* const stg = w < 4 ? smem + 2 * BLK + w * SB : smem + 2 * kRing * BLK + (w - 4) * SB;
+  E* o_rows = nullptr;      // the finished item's first row of this wave (uniform)
+  float* lse_rows = nullptr;
+  int o_nrows = 0;          // its rows below N (uniform)
+  float lse_out = 0.0f;
+  auto finish = [&]() {
+    float l;
+    if constexpr (ROWSUM_MFMA)
+      l = lacc[0];
+    else
+      l = pair_reduce(lsum, [](float x, float y) { return x + y; });
+    const float le = pair_reduce(lexact, [](float x, float y) { return x + y; });
+    const float inv = l > 0.0f ? a.o_scale / l : 0.0f;
+    // (the lane's row, opaque here: its addresses are formed here, not
+    // hoisted out of the item loop to hold registers through it)
+    int sr = ln;
+    asm volatile("" : "+v"(sr));
 #pragma unroll
-    for (int mt = 0; mt < NMT; ++mt) {
+    for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         ev4 ov;
 #pragma unroll
         for (int u = 0; u < 4; ++u) ov[u] = (E)(oacc[mt][4 * g + u] * inv);
-        *(ev4*)(O + 32 * mt + 8 * g + 4 * hf) = ov;
+        *(ev4*)(stg + sr * RB + 16 * ((4 * mt + g) ^ (sr % CPR)) + 8 * hf) = ov;
       }
+    const int wq0 = q0 + 32 * w;
+    o_rows = (E*)a.o + head + (size_t)wq0 * D;
+    lse_rows = a.lse == nullptr ? nullptr : a.lse + (size_t)bh * N + wq0;
+    o_nrows = max(0, min(32, N - wq0));
+    lse_out = le > 0.0f ? a.lse_scale * st.ref + (__logf(le) - (float)Elem16<E>::kPreLog2 * 0.69314718f)
+                        : -__builtin_inff();
+    count_tiles<X, FB_AUTO>(a, st, lane, qrow);
+  };
+  auto flush = [&]() {
+    constexpr int RPI = 64 / CPR;   // rows per instruction
+    int L = lane;
+    asm volatile("" : "+v"(L));     // as in finish()
+#pragma unroll
+    for (int k = 0; k < 32 / RPI; ++k) {
+      const int r = k * RPI + L / CPR, cc = L % CPR;
+      const ev8 v = *(const ev8*)(stg + r * RB + 16 * (cc ^ (r % CPR)));
+      if (r < o_nrows) *(ev8*)(o_rows + (size_t)r * D + 8 * cc) = v;
     }
-    if (a.lse != nullptr && hf == 0)
-      a.lse[(size_t)bh * N + qrow] =
-          le > 0.0f ? a.lse_scale * st.ref + (__logf(le) - (float)Elem16<E>::kPreLog2 * 0.69314718f)
-                    : -__builtin_inff();
+    if (lse_rows != nullptr && hf == 0 && ln < o_nrows) lse_rows[ln] = lse_out;
+  };
+
+  int it = item_of(0, gid, nwg);
+  set_item(it);
+  bool pref = false;   // this item's first blocks are in the rings already
+  for (int round = 0;; ++round) {
+    const int it_next = item_of(round + 1, gid, nwg);
+    set_next(it_next);
+    // ---- prologue: Q, and K_0..K_3, V_0, V_1 into the rings (unless the
+    // last item's steps loaded them)
+    if (!pref) {
+      load_q(head, qrow, qvalid);
+#pragma unroll
+      for (int j = 0; j < kKAhead; ++j) load_k(j, Int<0>());
+#pragma unroll
+      for (int j = 0; j < kVAhead; ++j) load_v(j, Int<0>());
+    }
+    step_barrier<0>();
+    // the same wait in a form the compiler sees: the Q fragments (plain global
+    // loads) are complete from here on, so no wait for them lands in the loop
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0), expcnt and lgkmcnt untouched
+    if (round > 0) flush();   // the previous item's O and lse
+
+    row_state_init(st, X == 1);
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) oacc[mt] = f32x16{};
+    lsum = 0.0f;
+    lacc = f32x16{};
+    lexact = 0.0f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) P[0][t] = P[1][t] = ev8{};
+    S[0][0] = S[0][1] = S[1][0] = S[1][1] = f32x16{};
+    if (jend_w > 0) qk(0, S[0][0], S[0][1]);
+    // step 0 refills K_0's slot: every wave must be done reading it (the
+    // stores just issued may stay in flight)
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+
+    // steady steps in groups of 4 (constant ring slots); only a group whose
+    // loads reach past the item's last block takes the crossing loads
+    int j = 0;
+    edge_step(j++);
+    for (; j + 8 <= jend_w; j += 4) {
+      steady_step(Int<0>(), j, Int<0>());
+      steady_step(Int<1>(), j + 1, Int<0>());
+      steady_step(Int<2>(), j + 2, Int<0>());
+      steady_step(Int<3>(), j + 3, Int<0>());
+    }
+    if (j + 4 < jend_w) {
+      steady_step(Int<0>(), j, Int<1>());
+      steady_step(Int<1>(), j + 1, Int<1>());
+      steady_step(Int<2>(), j + 2, Int<1>());
+      steady_step(Int<3>(), j + 3, Int<1>());
+      j += 4;
+    }
+    // two more steady steps when both qualify (j + 1 < jend_w): j is 1 mod 4
+    // here, so they take the group's first two slots, and after two steps the
+    // register sets are back where the edge steps expect them
+    if (j + 2 < jend_w) {
+      steady_step(Int<0>(), j, Int<1>());
+      steady_step(Int<1>(), j + 1, Int<1>());
+      j += 2;
+    }
+    for (; j <= jend; ++j) edge_step(j);
+    // the last steps' loads (zeros past the item's last block) still write
+    // LDS, V slots 2 and 3 among them: let every wave's land before the O
+    // staging there, the next item's loads or the end of the workgroup
+    if (!pref_next) asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+
+    finish();
+    if (it_next >= nitems) {
+      flush();
+      break;
+    }
+    pref = pref_next;
+    it = it_next;
+    set_item(it);
   }
-  count_tiles<X, FB_AUTO>(a, st, lane, qrow);
 }
 
 // ---------------------------------------------------------------------------

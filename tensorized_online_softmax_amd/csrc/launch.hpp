@@ -14,6 +14,25 @@ struct KernelChoice {
   bool fb_auto;      // fallback AUTO (x > 1 only)
 };
 
+// Workgroups of a persistent launch over `nitems` items: one per compute unit
+// of the current device (the kernels fill a compute unit with one workgroup),
+// rounded down to a multiple of 8 (the XCD count) when there are more items
+// than compute units.  The count is read once per device.
+inline int persistent_grid(int nitems) {
+  static int cus[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = -1;
+  int n = dev >= 0 ? cus[dev] : 0;
+  if (n <= 0) {
+    if (dev < 0 || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    if (dev >= 0) cus[dev] = n;
+  }
+  if (nitems <= n) return nitems;
+  return n >= 8 ? n & ~7 : n;
+}
+
 // Each returns hipSuccess, hipErrorNotSupported for a combination that has no
 // instance, or the launch error.
 hipError_t launch_bf16(const FwdArgs& a, const KernelChoice& k, hipStream_t stream);

@@ -9,7 +9,7 @@ template <typename E, int D, bool CAUSAL, int X, bool RS, bool FB>
 static hipError_t go_h16(const FwdArgs& a, hipStream_t s) {
   FwdArgs arg = a;
   arg.nqb = (a.N + kPBr - 1) / kPBr;
-  const dim3 grid((unsigned)arg.BH * (unsigned)arg.nqb), block(kPThreads);
+  const dim3 grid((unsigned)persistent_grid(arg.BH * arg.nqb)), block(kPThreads);
   // hipLaunchKernel reports this launch's own status (hipGetLastError could
   // return an error left behind by an earlier, unrelated call)
   void* params[] = {&arg};
