@@ -1,10 +1,11 @@
 // attn_fwd_fp8.hpp -- the fused attention forward kernel for OCP fp8 e4m3
 // inputs on gfx950 (v_mfma_scale_f32_32x32x64_f8f6f4 for both products).
 //
-// Same method and workgroup shape as the bf16 kernel (8 waves = 256 query
-// rows, 64-key blocks streamed through LDS rings by direct-to-LDS loads, the
-// tensorized online softmax of FlashAttention-T, section A2, Algorithm 1,
-// with the optional per-row fallback of "numerical stability guarantees").
+// Same method, workgroup shape and persistent item loop as the 16-bit kernel
+// (8 waves = 256 query rows, 64-key blocks streamed through LDS rings by
+// direct-to-LDS loads, O stored through LDS as whole rows, the tensorized
+// online softmax of FlashAttention-T, section A2, Algorithm 1, with the
+// optional per-row fallback of "numerical stability guarantees").
 // What differs for fp8:
 //   * Q, K, V are e4m3 codes with per-tensor fp32 descales; the logit scale
 //     c = scale * log2(e) * q_descale * k_descale, and O is multiplied by
@@ -64,44 +65,78 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_fp8(FwdArgs a) {
   constexpr int NMT = D / 32;                 // 32-row M tiles of O^T
   constexpr int NV_STEP = 2 * CHW;
   static_assert(CHW == 1, "one load instruction per wave and tensor");
-  __shared__ __attribute__((aligned(1024))) char smem[2 * kRing * BLK];
+  // Past the rings, 8 x 32 rows of bf16 O staging (one area per wave), as in
+  // the 16-bit kernel: O leaves through LDS as whole rows.
+  constexpr int ORB = 2 * D;                  // bytes per O row (bf16)
+  constexpr int SB = 32 * ORB;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kRing * BLK + kPWaves * SB];
   char* vring = smem;
 
   const int tid = threadIdx.x, lane = tid & 63, ln = lane & 31, hf = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int bid = blockIdx.x;
-  const int bh = bid % a.BH;
-  const int qb = CAUSAL ? (a.nqb - 1 - bid / a.BH) : bid / a.BH;
-  const int q0 = qb * kPBr;
+  // Persistent workgroups over items, as in the 16-bit kernel (item_of).
   const int N = a.N;
-  const int qrow = q0 + 32 * w + ln;
-  const bool qvalid = qrow < N;
-  const size_t head = (size_t)bh * N * D;
-  const unsigned char* Q = (const unsigned char*)a.q + head;
-  const u32x4 kdesc = buffer_desc((const unsigned char*)a.k + head, (unsigned)N * RB);
-  const u32x4 vdesc = buffer_desc((const unsigned char*)a.v + head, (unsigned)N * RB);
-
   const int nblk = (N + kBc - 1) / kBc;
-  const int qlast_wg = min(q0 + kPBr, N) - 1;
-  const int jend = CAUSAL ? qlast_wg / kBc + 1 : nblk;
-  const int wq0 = q0 + 32 * w;
-  const int wqlast = min(wq0 + 31, N - 1);
-  const int jend_w = (wq0 >= N) ? 0 : (CAUSAL ? wqlast / kBc + 1 : nblk);
-  const int klim = qvalid ? (CAUSAL ? qrow + 1 : N) : 0;
+  const int nitems = a.BH * a.nqb;
+  const int nwg = gridDim.x, gid = blockIdx.x;
+  auto item_jend = [&](int q0_) { return CAUSAL ? (min(q0_ + kPBr, N) - 1) / kBc + 1 : nblk; };
+
+  int bh = 0, q0 = 0, qrow = 0, jend = 0, jend_w = 0, klim = 0;
+  bool qvalid = false;
+  size_t head = 0;
+  u32x4 kdesc = {}, vdesc = {};
+  auto set_item = [&](int it) {
+    int qb;
+    item_coords(a, CAUSAL, it, bh, qb);
+    q0 = qb * kPBr;
+    qrow = q0 + 32 * w + ln;
+    qvalid = qrow < N;
+    head = (size_t)bh * N * D;
+    kdesc = buffer_desc((const unsigned char*)a.k + head, (unsigned)N * RB);
+    vdesc = buffer_desc((const unsigned char*)a.v + head, (unsigned)N * RB);
+    jend = item_jend(q0);
+    const int wq0 = q0 + 32 * w;
+    jend_w = (wq0 >= N) ? 0 : (CAUSAL ? min(wq0 + 31, N - 1) / kBc + 1 : nblk);
+    klim = qvalid ? (CAUSAL ? qrow + 1 : N) : 0;
+  };
+  // the next item's first K and V blocks ride on this item's last steps when
+  // this item's block count is a multiple of the ring size; its Q is loaded
+  // in this item's last step
+  bool pref_next = false;
+  int jend_n = 0, qrow_n = 0;
+  bool qvalid_n = false;
+  size_t head_n = 0;
+  u32x4 kdesc_n = {}, vdesc_n = {};
+  auto set_next = [&](int it) {
+    pref_next = it < nitems && jend % kRing == 0;
+    if (pref_next) {
+      int bh_n, qb_n;
+      item_coords(a, CAUSAL, it, bh_n, qb_n);
+      head_n = (size_t)bh_n * N * D;
+      kdesc_n = buffer_desc((const unsigned char*)a.k + head_n, (unsigned)N * RB);
+      vdesc_n = buffer_desc((const unsigned char*)a.v + head_n, (unsigned)N * RB);
+      jend_n = item_jend(qb_n * kPBr);
+      qrow_n = qb_n * kPBr + 32 * w + ln;
+      qvalid_n = qrow_n < N;
+    }
+  };
 
   // Q^T operand of k-step kk: lane (query ln, half hf) holds Q[qrow][64 kk + 32 hf + 0..31]
   i32x8 qf[2];
+  auto load_q = [&](size_t head_, int qrow_, bool qvalid_) {
+    const unsigned char* Q = (const unsigned char*)a.q + head_;
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk) {
-    if (qvalid) {
-      const u32x4* src = (const u32x4*)(Q + (size_t)qrow * D + 64 * kk + 32 * hf);
-      const u32x4 lo = src[0], hi = src[1];
-      qf[kk] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                     (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-    } else {
-      qf[kk] = i32x8{};
+    for (int kk = 0; kk < 2; ++kk) {
+      if (qvalid_) {
+        const u32x4* src = (const u32x4*)(Q + (size_t)qrow_ * D + 64 * kk + 32 * hf);
+        const u32x4 lo = src[0], hi = src[1];
+        qf[kk] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                       (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      } else {
+        qf[kk] = i32x8{};
+      }
     }
-  }
+  };
 
   // direct-to-LDS loads: lane L of wave w fills bytes [1024 w + 16 L, +16) of
   // the slot = row 8w + L/8, chunk position L%8, fetching the chunk that the
@@ -114,11 +149,23 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_fp8(FwdArgs a) {
   }
   const unsigned lds0 = (unsigned)(unsigned long long)(__attribute__((address_space(3))) char*)smem;
   const unsigned vdst = lds0 + (unsigned)w * 1024, kdst = vdst + kRing * BLK;
-  auto load_k = [&](int j) {
-    dma_block<CHW>(block_desc(kdesc, j, jend, BLK), kdst + (j % kRing) * BLK, kgoff);
+  // block j of the item's K (V), zeros past its end; with XING the blocks past
+  // the end are the next item's first ones when those are prefetched
+  auto ring_desc = [&](const u32x4& cur, const u32x4& nxt, int j) -> u32x4 {
+    return select_desc(pref_next & (j >= jend), block_desc(nxt, j - jend, jend_n, BLK),
+                       block_desc(cur, j, jend, BLK));
   };
-  auto load_v = [&](int j) {
-    dma_block<CHW>(block_desc(vdesc, j, jend, BLK), vdst + (j % kRing) * BLK, vgoff);
+  auto load_k = [&](int j, auto XING) {
+    if constexpr (decltype(XING)::value)
+      dma_block<CHW>(ring_desc(kdesc, kdesc_n, j), kdst + (j % kRing) * BLK, kgoff);
+    else
+      dma_block<CHW>(block_desc(kdesc, j, jend, BLK), kdst + (j % kRing) * BLK, kgoff);
+  };
+  auto load_v = [&](int j, auto XING) {
+    if constexpr (decltype(XING)::value)
+      dma_block<CHW>(ring_desc(vdesc, vdesc_n, j), vdst + (j % kRing) * BLK, vgoff);
+    else
+      dma_block<CHW>(block_desc(vdesc, j, jend, BLK), vdst + (j % kRing) * BLK, vgoff);
   };
 
   // K operand of tile u, k-step kk: lane (key ln, half hf) reads the 32 bytes
@@ -140,13 +187,14 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_fp8(FwdArgs a) {
   }
 
   RowState st;
-  row_state_init(st, X == 1);
   const float c = a.c, tau = a.tau;
   f32x16 oacc[NMT];
-#pragma unroll
-  for (int mt = 0; mt < NMT; ++mt) oacc[mt] = f32x16{};
-  f32x16 lacc = {};     // row sum of hi + lo of 2^8 P~ (MFMA; every register holds it)
-  float lexact = 0.0f;  // row sum of the unrounded 2^8 P~ (this lane's keys only)
+  f32x16 lacc;      // row sum of hi + lo of 2^8 P~ (MFMA; every register holds it)
+  float lexact;     // row sum of the unrounded 2^8 P~ (this lane's keys only)
+  // pipeline registers: entering step j, S_j in S[0] and the hi and lo terms
+  // of P~_{j-1} in PH[1], PL[1] (the steady steps alternate the two sets)
+  f32x16 S[2][2];
+  i32x8 PH[2], PL[2];
   const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
                       0x38383838, 0x38383838, 0x38383838, 0x38383838};   // e4m3 1.0
 
@@ -249,32 +297,21 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_fp8(FwdArgs a) {
       lacc *= alpha;
     }
   };
-  auto step_loads = [&](int j) {
-    load_k(j + kKAhead);
-    load_v(j + kVAhead);
+  auto step_loads = [&](int j, auto XING) {
+    load_k(j + kKAhead, XING);
+    load_v(j + kVAhead, XING);
   };
 
-  // ---- prologue: K_0..K_3 and V_0, V_1 into the rings, then S_0
-#pragma unroll
-  for (int j = 0; j < kKAhead; ++j) load_k(j);
-#pragma unroll
-  for (int j = 0; j < kVAhead; ++j) load_v(j);
-  step_barrier<0>();
-  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0), as the compiler sees it (Q loaded)
-
-  // Pipeline of key block b (as in the bf16 kernel): S_b = K_b Q^T in step b-1;
-  // its tile maximum, exponentials and row sums in step b, where O is rescaled
-  // by alpha_b at the end; P~_b V_b in step b+1.  Entering step j: S_j in S[0],
-  // the hi and lo terms of P~_{j-1} in PH[1], PL[1].
-  f32x16 S[2][2];
-  i32x8 PH[2], PL[2];
-  S[0][0] = S[0][1] = S[1][0] = S[1][1] = f32x16{};
-  PH[0] = PH[1] = PL[0] = PL[1] = i32x8{};
-  if (jend_w > 0) qk(0, S[0][0], S[0][1]);
-  step_barrier<0>();   // step 0 refills K_0's slot
-
+  // Pipeline of key block b (as in the 16-bit kernel): S_b = K_b Q^T in step
+  // b-1; its tile maximum, exponentials and row sums in step b, where O is
+  // rescaled by alpha_b at the end; P~_b V_b in step b+1.  The last step
+  // (j = jend) loads the next item's Q instead of K and V when the next item
+  // is prefetched.
   auto edge_step = [&](int j) {
-    step_loads(j);
+    if (pref_next && j == jend)
+      load_q(head_n, qrow_n, qvalid_n);
+    else
+      step_loads(j, Int<1>());
     float alpha = 1.0f, nb = 0.0f;
     if (j < jend_w) {
       if (j == jend_w - 1) mask_block(j, S[0][0], S[0][1]);
@@ -304,12 +341,12 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_fp8(FwdArgs a) {
   //                 with the 8 exponential units of S_j in the first 8
   // Constant ring slots (four steps per loop iteration); S and P~ alternate
   // between the two register sets.
-  auto steady_step = [&](auto U, int j) {
+  auto steady_step = [&](auto U, int j, auto XING) {
     constexpr int u = decltype(U)::value;
     constexpr int cur = u & 1, nxt = cur ^ 1;
     constexpr int kslot = (u + 2) % kRing, vslot = u % kRing;   // K_{j+1}, V_{j-1}
     f32x16 &c0 = S[cur][0], &c1 = S[cur][1], &n0 = S[nxt][0], &n1 = S[nxt][1];
-    step_loads(j);
+    step_loads(j, XING);
     float alpha = 1.0f, nb = 0.0f;
     pe[0] = pe[1] = 0.0f;
     // phase A: QK g = 2 kk + t, operands read one instruction ahead
@@ -354,40 +391,113 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_fp8(FwdArgs a) {
     rescale(alpha);
   };
 
-  int j = 0;
-  edge_step(j++);
-  for (; j + 4 < jend_w; j += 4) {
-    steady_step(Int<0>(), j);
-    steady_step(Int<1>(), j + 1);
-    steady_step(Int<2>(), j + 2);
-    steady_step(Int<3>(), j + 3);
-  }
-  for (; j <= jend; ++j) edge_step(j);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-
-  // ---- epilogue: O / l (l: the sum of hi + lo, so the 2^8 cancels), and
-  // lse = lse_scale * ref + ln(l_exact / 2^8)
-  const float l = lacc[0];
-  const float le = pair_reduce(lexact, [](float x, float y) { return x + y; });
-  const float inv = l > 0.0f ? a.o_scale / l : 0.0f;
-  if (qvalid) {
-    __bf16* O = (__bf16*)a.o + head + (size_t)qrow * D;
+  // ---- epilogue of an item: O / l (l: the sum of hi + lo, so the 2^8
+  // cancels), lse = lse_scale * ref + ln(l_exact / 2^8).  finish() puts this
+  // wave's O rows in its staging area (chunk c of row r at c xor (r mod 16));
+  // flush() stores them as whole rows after the next item's prologue wait.
+  constexpr int CPR = ORB / 16;
+  char* const stg = smem + 2 * kRing * BLK + w * SB;
+  __bf16* o_rows = nullptr;
+  float* lse_rows = nullptr;
+  int o_nrows = 0;
+  float lse_out = 0.0f;
+  auto finish = [&]() {
+    const float l = lacc[0];
+    const float le = pair_reduce(lexact, [](float x, float y) { return x + y; });
+    const float inv = l > 0.0f ? a.o_scale / l : 0.0f;
+    int sr = ln;
+    asm volatile("" : "+v"(sr));   // addresses formed here, not hoisted
 #pragma unroll
-    for (int mt = 0; mt < NMT; ++mt) {
+    for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         bf16x4 ov;
 #pragma unroll
         for (int u = 0; u < 4; ++u) ov[u] = (__bf16)(oacc[mt][4 * g + u] * inv);
-        *(bf16x4*)(O + 32 * mt + 8 * g + 4 * hf) = ov;
+        *(bf16x4*)(stg + sr * ORB + 16 * ((4 * mt + g) ^ (sr % CPR)) + 8 * hf) = ov;
       }
+    const int wq0 = q0 + 32 * w;
+    o_rows = (__bf16*)a.o + head + (size_t)wq0 * D;
+    lse_rows = a.lse == nullptr ? nullptr : a.lse + (size_t)bh * N + wq0;
+    o_nrows = max(0, min(32, N - wq0));
+    lse_out = le > 0.0f ? a.lse_scale * st.ref + (__logf(le) - (float)kF8PreScaleLog2 * 0.69314718f)
+                        : -__builtin_inff();
+    count_tiles<X, FB_AUTO>(a, st, lane, qrow);
+  };
+  auto flush = [&]() {
+    constexpr int RPI = 64 / CPR;
+    int L = lane;
+    asm volatile("" : "+v"(L));
+#pragma unroll
+    for (int k = 0; k < 32 / RPI; ++k) {
+      const int r = k * RPI + L / CPR, cc = L % CPR;
+      const u32x4 v = *(const u32x4*)(stg + r * ORB + 16 * (cc ^ (r % CPR)));
+      if (r < o_nrows) *(u32x4*)(o_rows + (size_t)r * D + 8 * cc) = v;
     }
-    if (a.lse != nullptr && hf == 0)
-      a.lse[(size_t)bh * N + qrow] =
-          le > 0.0f ? a.lse_scale * st.ref + (__logf(le) - (float)kF8PreScaleLog2 * 0.69314718f)
-                    : -__builtin_inff();
+    if (lse_rows != nullptr && hf == 0 && ln < o_nrows) lse_rows[ln] = lse_out;
+  };
+
+  int it = item_of(0, gid, nwg);
+  set_item(it);
+  bool pref = false;
+  for (int round = 0;; ++round) {
+    const int it_next = item_of(round + 1, gid, nwg);
+    set_next(it_next);
+    if (!pref) {
+      load_q(head, qrow, qvalid);
+#pragma unroll
+      for (int j = 0; j < kKAhead; ++j) load_k(j, Int<0>());
+#pragma unroll
+      for (int j = 0; j < kVAhead; ++j) load_v(j, Int<0>());
+    }
+    step_barrier<0>();
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0), as the compiler sees it (Q loaded)
+    if (round > 0) flush();
+
+    row_state_init(st, X == 1);
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) oacc[mt] = f32x16{};
+    lacc = f32x16{};
+    lexact = 0.0f;
+    S[0][0] = S[0][1] = S[1][0] = S[1][1] = f32x16{};
+    PH[0] = PH[1] = PL[0] = PL[1] = i32x8{};
+    if (jend_w > 0) qk(0, S[0][0], S[0][1]);
+    // step 0 refills K_0's slot (the O stores may stay in flight)
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+
+    int j = 0;
+    edge_step(j++);
+    for (; j + 8 <= jend_w; j += 4) {
+      steady_step(Int<0>(), j, Int<0>());
+      steady_step(Int<1>(), j + 1, Int<0>());
+      steady_step(Int<2>(), j + 2, Int<0>());
+      steady_step(Int<3>(), j + 3, Int<0>());
+    }
+    if (j + 4 < jend_w) {
+      steady_step(Int<0>(), j, Int<1>());
+      steady_step(Int<1>(), j + 1, Int<1>());
+      steady_step(Int<2>(), j + 2, Int<1>());
+      steady_step(Int<3>(), j + 3, Int<1>());
+      j += 4;
+    }
+    if (j + 2 < jend_w) {
+      steady_step(Int<0>(), j, Int<1>());
+      steady_step(Int<1>(), j + 1, Int<1>());
+      j += 2;
+    }
+    for (; j <= jend; ++j) edge_step(j);
+    // zero loads past the item's end land before the next item reuses the slots
+    if (!pref_next) asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+
+    finish();
+    if (it_next >= nitems) {
+      flush();
+      break;
+    }
+    pref = pref_next;
+    it = it_next;
+    set_item(it);
   }
-  count_tiles<X, FB_AUTO>(a, st, lane, qrow);
 }
 
 }  // namespace tos

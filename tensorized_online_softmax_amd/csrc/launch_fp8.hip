@@ -8,7 +8,7 @@ template <bool CAUSAL, int X, bool FB>
 static hipError_t go(const FwdArgs& a, hipStream_t s) {
   FwdArgs arg = a;
   arg.nqb = (a.N + kPBr - 1) / kPBr;
-  const dim3 grid((unsigned)arg.BH * (unsigned)arg.nqb), block(kPThreads);
+  const dim3 grid((unsigned)persistent_grid(arg.BH * arg.nqb)), block(kPThreads);
   void* params[] = {&arg};
   return hipLaunchKernel(reinterpret_cast<const void*>(&attn_fwd_fp8<CAUSAL, X, FB>), grid, block, params, 0, s);
 }
