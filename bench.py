@@ -188,6 +188,66 @@ def grid_sweep(dtypes, steps, warmup):
         del q, k, v, o, lse, inp
 
 
+# The ablation's knob settings, after FlashAttention-T's evaluation (section
+# A4, Fig 9 and Fig 10: FA2, FA2 + Max16, AllTensor, FA-T): name, X, row-sum
+# split, schedule.  The pages' AllTensor (scaling and FMA on the tensor unit)
+# has no counterpart here: gfx950 has no TF32 matrix instruction.
+ABLATION = [
+    ("per_row_sequential", 1, "valu", "sequential"),     # FA2 analog
+    ("per_row_cosched", 1, "valu", "cosched"),
+    ("tile16_cosched", 16, "valu", "cosched"),           # Max16 analog
+    ("tile32_sequential", 32, "valu", "sequential"),
+    ("tile32_cosched", 32, "valu", "cosched"),           # FA-T analog (the default)
+    ("tile32_rowsum_mfma", 32, "rowsum_mfma", "cosched"),
+]
+
+
+def ablation(workload, steps, warmup, reps=3):
+    """Median launch time of each knob setting on one workload.  Each setting
+    runs in blocks (a few warmup launches, then timed ones) so that it is
+    measured at its own power and clock state, and the round of blocks repeats
+    `reps` times so that drift falls on every setting alike.  (Alternating the
+    settings launch by launch instead lets a low-power neighbour raise the
+    clock of the next launch.)"""
+    import torch
+    from tensorized_online_softmax_amd import binding, inputs
+    w = inputs.WORKLOADS[workload]
+    if w.dtype not in ("bf16", "f16"):
+        raise SystemExit("the ablation runs the 16-bit kernels")
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    inp = inputs.make_workload(w)
+    q, k, v = (inp[n].cuda() for n in ("q", "k", "v"))
+    odt = torch.float16 if w.dtype == "f16" else torch.bfloat16
+    o = torch.empty((w.B, w.H, w.N, w.d), dtype=odt, device="cuda")
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
+    per_block = max(3, min(steps, 60) // reps)
+    warm = max(2, min(warmup, 5))
+    times = [[] for _ in ABLATION]
+    for _ in range(reps):
+        for si, (name, x, split, sched) in enumerate(ABLATION):
+            def f():
+                binding.attn_fwd(q, k, v, causal=w.causal, scale=w.scale, dtype=w.dtype,
+                                 x_tile=x, split=split, schedule=sched, out=o, lse=lse)
+            for _ in range(warm):
+                f()
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(per_block)]
+            for a, b in ev:
+                a.record(stream)
+                f()
+                b.record(stream)
+            torch.cuda.synchronize()
+            times[si] += [a.elapsed_time(b) / 1e3 for a, b in ev]
+    med = [sorted(t)[len(t) // 2] for t in times]
+    for (name, x, split, sched), m, t in zip(ABLATION, med, times):
+        tf = w.flops() / m / 1e12
+        print(json.dumps({"workload": w.name, "setting": name, "x_tile": x, "softmax_split": split,
+                          "schedule": sched, "launches": len(t), "median_us": round(m * 1e6, 2),
+                          "tflops": round(tf, 1), "frac": round(tf / PEAK_TFLOPS[w.dtype], 4),
+                          "speedup_over_first": round(med[0] / m, 4)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -195,6 +255,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="causal_bf16")
     ap.add_argument("--split", default="valu", choices=["valu", "rowsum_mfma"])
+    ap.add_argument("--schedule", default="cosched", choices=["cosched", "sequential"],
+                    help="sequential: the no-co-scheduling ablation (16-bit inputs)")
+    ap.add_argument("--ablation", action="store_true",
+                    help="instead of the attention bench: time the knob settings of the "
+                         "ablation (X, row-sum split, schedule) on the workload, alternating "
+                         "them launch by launch; one JSON line per setting")
     ap.add_argument("--x-tile", type=int, default=None)
     ap.add_argument("--fallback", default=None, choices=["off", "auto", "force"],
                     help="default: the workload's own (AUTO for the fp8 stress workload)")
@@ -215,6 +281,9 @@ def main():
         return
     if args.grid:
         grid_sweep(args.grid.split(","), args.steps, args.warmup)
+        return
+    if args.ablation:
+        ablation(args.workload, args.steps, args.warmup)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -242,7 +311,7 @@ def main():
     def step():
         binding.attn_fwd(q, k, v, causal=w.causal, scale=w.scale, dtype=w.dtype,
                          x_tile=x_tile, split=args.split, fallback=fallback,
-                         descale=descale, out=o, lse=lse)
+                         descale=descale, out=o, lse=lse, schedule=args.schedule)
 
     for _ in range(args.warmup):
         step()
@@ -304,6 +373,7 @@ def main():
                    "causal": w.causal, "x_tile": x_tile,
                    # e4m3 P~ pairs have no vector dot form: fp8 sums them on the matrix unit
                    "softmax_split": "rowsum_mfma" if w.dtype == "fp8" else args.split,
+                   "schedule": args.schedule,
                    "fallback": fallback, "Br": 128 if w.dtype == "f32" else 256, "Bc": 64,
                    "flops_per_step": flops, "pct_of_peak": round(100 * achieved / peak, 2)},
         "roofline": roofline,

@@ -72,6 +72,21 @@ typedef enum {
  * unrounded fp32 sum gives lse.  TOS_FP8_E4M3 has no vector form for e4m3
  * pairs: its rounded sum is always the matrix-unit one, whatever the option. */
 
+/* Instruction schedule of the 16-bit kernels (an ablation of FlashAttention-T
+ * section A2, "tensor-vector parallelism", Fig 7, and of its evaluation, Fig 9
+ * and Fig 10). */
+typedef enum {
+    TOS_SCHEDULE_COSCHED = 0,    /* matrix and vector work of consecutive key
+                                    blocks interleaved in one instruction stream
+                                    (the default)                                    */
+    TOS_SCHEDULE_SEQUENTIAL = 1  /* each key block's softmax, then the next block's
+                                    QK^T, then the previous block's P~V, one after
+                                    another; overlap only across the waves of a
+                                    SIMD.  bf16 and f16 only, with the vector row
+                                    sum, no AUTO fallback and X = 1 or 32; other
+                                    combinations return TOS_ERR_UNSUPPORTED         */
+} tos_schedule;
+
 /* All-underflow handling (FlashAttention-T section A2, "numerical stability
  * guarantees": an implementation may fall back to per-row computation). */
 typedef enum {
@@ -97,6 +112,7 @@ typedef struct {
     int* fallback_tiles;   /* NULL, or a device int the kernels add to, once per
                               X-row tile that ran with per-row maxima (AUTO switch
                               or FORCE).  The caller zeroes it.                    */
+    int schedule;          /* a tos_schedule value                                  */
 } tos_fwd_opts;
 
 /*

@@ -15,6 +15,7 @@ TOS_OK, TOS_ERR_INVALID_ARG, TOS_ERR_UNSUPPORTED, TOS_ERR_HIP = 0, 1, 2, 3
 TOS_F32, TOS_BF16, TOS_FP8_E4M3, TOS_F16 = 0, 1, 2, 3
 TOS_SPLIT_VALU, TOS_SPLIT_ROWSUM_MFMA = 0, 1
 TOS_FALLBACK_OFF, TOS_FALLBACK_AUTO, TOS_FALLBACK_FORCE = 0, 1, 2
+TOS_SCHEDULE_COSCHED, TOS_SCHEDULE_SEQUENTIAL = 0, 1
 
 EXPORTED = ("tos_attn_fwd", "tos_fwd_opts_default", "tos_attn_fwd_flops",
             "tos_status_string", "tos_version")
@@ -25,7 +26,7 @@ class tos_fwd_opts(ctypes.Structure):
                 ("softmax_split", ctypes.c_int), ("fallback", ctypes.c_int),
                 ("fallback_tau", ctypes.c_float), ("q_descale", ctypes.c_float),
                 ("k_descale", ctypes.c_float), ("v_descale", ctypes.c_float),
-                ("fallback_tiles", ctypes.c_void_p)]
+                ("fallback_tiles", ctypes.c_void_p), ("schedule", ctypes.c_int)]
 
 
 class TosError(RuntimeError):
@@ -112,10 +113,11 @@ def tos_version():
 _DTYPE_CODES = {"f32": TOS_F32, "bf16": TOS_BF16, "fp8": TOS_FP8_E4M3, "f16": TOS_F16}
 _SPLITS = {"valu": TOS_SPLIT_VALU, "rowsum_mfma": TOS_SPLIT_ROWSUM_MFMA}
 _FALLBACKS = {"off": TOS_FALLBACK_OFF, "auto": TOS_FALLBACK_AUTO, "force": TOS_FALLBACK_FORCE}
+_SCHEDULES = {"cosched": TOS_SCHEDULE_COSCHED, "sequential": TOS_SCHEDULE_SEQUENTIAL}
 
 
 def make_opts(x_tile=32, split="valu", fallback="off", tau=0.0, descale=None,
-              fallback_tiles=None):
+              fallback_tiles=None, schedule="cosched"):
     op = tos_fwd_opts_default()
     op.x_tile = int(x_tile)
     op.softmax_split = _SPLITS[split]
@@ -124,12 +126,13 @@ def make_opts(x_tile=32, split="valu", fallback="off", tau=0.0, descale=None,
     if descale is not None:
         op.q_descale, op.k_descale, op.v_descale = (float(descale[n]) for n in ("q", "k", "v"))
     op.fallback_tiles = _ptr(fallback_tiles)
+    op.schedule = _SCHEDULES[schedule]
     return op
 
 
 def attn_fwd(q, k, v, causal=False, scale=None, dtype=None, x_tile=32, split="valu",
              fallback="off", tau=0.0, descale=None, with_lse=True, fallback_tiles=None,
-             out=None, lse=None, stream=None):
+             out=None, lse=None, stream=None, schedule="cosched"):
     """Allocate O (and lse) with torch and run tos_attn_fwd on the current stream.
 
     q, k, v: contiguous CUDA tensors [B, H, N, d] of float32, bfloat16, float16
@@ -151,7 +154,7 @@ def attn_fwd(q, k, v, causal=False, scale=None, dtype=None, x_tile=32, split="va
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     if not with_lse:
         lse = None
-    op = make_opts(x_tile, split, fallback, tau, descale, fallback_tiles)
+    op = make_opts(x_tile, split, fallback, tau, descale, fallback_tiles, schedule)
     rc = tos_attn_fwd(q, k, v, o, lse, B, H, N, d, causal, scale, _DTYPE_CODES[dtype], op,
                       stream)
     if rc != TOS_OK:

@@ -274,7 +274,9 @@ template <typename T> __device__ __forceinline__ void pin(const T& x) {
 template <int I> struct Int { static constexpr int value = I; };
 
 
-template <typename E, int D, bool CAUSAL, int X, bool ROWSUM_MFMA, bool FB_AUTO>
+// SEQ: the sequential-schedule ablation -- every step is the generic step
+// (softmax, then QK^T, then P~V), with no interleaving inside a wave.
+template <typename E, int D, bool CAUSAL, int X, bool ROWSUM_MFMA, bool FB_AUTO, bool SEQ>
 __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_h16(FwdArgs a) {
   typedef typename Elem16<E>::v8 ev8;
   typedef typename Elem16<E>::v4 ev4;
@@ -750,26 +752,28 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_h16(FwdArgs a) {
     // loads reach past the item's last block takes the crossing loads
     int j = 0;
     edge_step(j++);
-    for (; j + 8 <= jend_w; j += 4) {
-      steady_step(Int<0>(), j, Int<0>());
-      steady_step(Int<1>(), j + 1, Int<0>());
-      steady_step(Int<2>(), j + 2, Int<0>());
-      steady_step(Int<3>(), j + 3, Int<0>());
-    }
-    if (j + 4 < jend_w) {
-      steady_step(Int<0>(), j, Int<1>());
-      steady_step(Int<1>(), j + 1, Int<1>());
-      steady_step(Int<2>(), j + 2, Int<1>());
-      steady_step(Int<3>(), j + 3, Int<1>());
-      j += 4;
-    }
-    // two more steady steps when both qualify (j + 1 < jend_w): j is 1 mod 4
-    // here, so they take the group's first two slots, and after two steps the
-    // register sets are back where the edge steps expect them
-    if (j + 2 < jend_w) {
-      steady_step(Int<0>(), j, Int<1>());
-      steady_step(Int<1>(), j + 1, Int<1>());
-      j += 2;
+    if constexpr (!SEQ) {
+      for (; j + 8 <= jend_w; j += 4) {
+        steady_step(Int<0>(), j, Int<0>());
+        steady_step(Int<1>(), j + 1, Int<0>());
+        steady_step(Int<2>(), j + 2, Int<0>());
+        steady_step(Int<3>(), j + 3, Int<0>());
+      }
+      if (j + 4 < jend_w) {
+        steady_step(Int<0>(), j, Int<1>());
+        steady_step(Int<1>(), j + 1, Int<1>());
+        steady_step(Int<2>(), j + 2, Int<1>());
+        steady_step(Int<3>(), j + 3, Int<1>());
+        j += 4;
+      }
+      // two more steady steps when both qualify (j + 1 < jend_w): j is 1 mod 4
+      // here, so they take the group's first two slots, and after two steps the
+      // register sets are back where the edge steps expect them
+      if (j + 2 < jend_w) {
+        steady_step(Int<0>(), j, Int<1>());
+        steady_step(Int<1>(), j + 1, Int<1>());
+        j += 2;
+      }
     }
     for (; j <= jend; ++j) edge_step(j);
     // the last steps' loads (zeros past the item's last block) still write

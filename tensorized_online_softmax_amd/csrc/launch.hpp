@@ -12,6 +12,7 @@ struct KernelChoice {
   int x;             // 1, 16 or 32
   bool rowsum_mfma;  // row sum on the matrix unit (fp8: always)
   bool fb_auto;      // fallback AUTO (x > 1 only)
+  bool seq = false;  // sequential schedule (16-bit kernels, x = 1 or 32, VALU row sum, no AUTO)
 };
 
 // Workgroups of a persistent launch over `nitems` items: one per compute unit

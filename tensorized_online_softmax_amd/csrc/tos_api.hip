@@ -86,6 +86,8 @@ tos_status tos_attn_fwd(const void* q, const void* k, const void* v, void* o, fl
       op.fallback != TOS_FALLBACK_FORCE)
     return TOS_ERR_INVALID_ARG;
   if (!std::isfinite(op.fallback_tau) || op.fallback_tau < 0.0f) return TOS_ERR_INVALID_ARG;
+  if (op.schedule != TOS_SCHEDULE_COSCHED && op.schedule != TOS_SCHEDULE_SEQUENTIAL)
+    return TOS_ERR_INVALID_ARG;
 
   // ---- sizes and scalars
   if (dtype != TOS_F32 && dtype != TOS_BF16 && dtype != TOS_FP8_E4M3 && dtype != TOS_F16)
@@ -127,7 +129,11 @@ tos_status tos_attn_fwd(const void* q, const void* k, const void* v, void* o, fl
   kc.rowsum_mfma = op.softmax_split == TOS_SPLIT_ROWSUM_MFMA;
   kc.x = op.fallback == TOS_FALLBACK_FORCE ? 1 : op.x_tile;
   kc.fb_auto = op.fallback == TOS_FALLBACK_AUTO && op.x_tile > 1;
+  kc.seq = op.schedule == TOS_SCHEDULE_SEQUENTIAL;
   if (dtype == TOS_F32 && kc.rowsum_mfma) return TOS_ERR_UNSUPPORTED;
+  if (kc.seq && ((dtype != TOS_BF16 && dtype != TOS_F16) || kc.rowsum_mfma || kc.fb_auto ||
+                 kc.x == 16))
+    return TOS_ERR_UNSUPPORTED;
   if (dtype == TOS_FP8_E4M3 && d != 128) return TOS_ERR_UNSUPPORTED;
 
   tos::FwdArgs a;
@@ -167,9 +173,9 @@ tos_status tos_attn_fwd(const void* q, const void* k, const void* v, void* o, fl
     e = tos::launch_fp8(a, kc, s);
   if (log_enabled())
     std::fprintf(stderr, "[tos] dtype=%d B=%lld H=%lld N=%lld d=%d causal=%d X=%d rowsum_mfma=%d "
-                 "fallback=%d grid=%lld: %s\n", (int)dtype, (long long)B, (long long)H,
+                 "fallback=%d sequential=%d items=%lld: %s\n", (int)dtype, (long long)B, (long long)H,
                  (long long)N, kc.d, (int)kc.causal, kc.x, (int)kc.rowsum_mfma, op.fallback,
-                 (long long)(BH * nqb), hipGetErrorString(e));
+                 (int)kc.seq, (long long)(BH * nqb), hipGetErrorString(e));
   if (e == hipErrorNotSupported) return TOS_ERR_UNSUPPORTED;
   return e == hipSuccess ? TOS_OK : TOS_ERR_HIP;
 }

@@ -95,6 +95,13 @@ def opts(**kw):
     (dict(dtype=tb.TOS_F32, opts=opts(softmax_split=1)), tb.TOS_ERR_UNSUPPORTED),
     (dict(dtype=tb.TOS_FP8_E4M3, d=64), tb.TOS_ERR_UNSUPPORTED),   # fp8: d = 128 only
     (dict(dtype=tb.TOS_F16, d=96), tb.TOS_ERR_UNSUPPORTED),
+    (dict(opts=opts(schedule=2)), tb.TOS_ERR_INVALID_ARG),
+    # the sequential schedule: 16-bit inputs, VALU row sum, no AUTO, X = 1 or 32
+    (dict(dtype=tb.TOS_F32, opts=opts(schedule=1)), tb.TOS_ERR_UNSUPPORTED),
+    (dict(dtype=tb.TOS_FP8_E4M3, opts=opts(schedule=1)), tb.TOS_ERR_UNSUPPORTED),
+    (dict(opts=opts(schedule=1, softmax_split=1)), tb.TOS_ERR_UNSUPPORTED),
+    (dict(opts=opts(schedule=1, x_tile=16)), tb.TOS_ERR_UNSUPPORTED),
+    (dict(opts=opts(schedule=1, fallback=1)), tb.TOS_ERR_UNSUPPORTED),
     (dict(dtype=4), tb.TOS_ERR_INVALID_ARG),
     (dict(B=70000, H=70000), tb.TOS_ERR_UNSUPPORTED),       # grid beyond 2^31
     # empty problems: nothing to do, and no pointer is needed
