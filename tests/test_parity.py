@@ -245,3 +245,34 @@ def test_grid_sampled(w):
         [b * w.N + i for b in (0, BH - 1) for i in (0, 1, 63, 64, 255, 256, w.N - 1)]]))
     o_ref, lse_ref = oracle_exact(inp, w.causal, rows=rows)
     assert_close(o[rows], o_ref, lse[rows], lse_ref, w.dtype, w.name)
+
+
+# Several items per persistent workgroup (more query blocks than compute
+# units), with block counts that are and are not multiples of the ring size:
+# the ring carried across items, the next Q loaded in the last step, the O
+# staging and the plain prologue after an item that could not prefetch.
+@pytest.mark.parametrize("dtype,B,H,N,d", [
+    ("bf16", 1, 300, 300, 64),     # 600 items, 5 blocks: no prefetch
+    ("bf16", 2, 160, 520, 128),    # 960 items, 9 blocks (3rd query block: 1)
+    ("bf16", 1, 130, 1000, 128),   # 520 items, 16 blocks: prefetch throughout
+    ("f16", 1, 300, 300, 128),
+    ("f16", 2, 150, 700, 64),
+    ("fp8", 1, 300, 300, 128),
+    ("fp8", 2, 160, 520, 128),
+])
+@pytest.mark.parametrize("causal", [False, True])
+def test_persistent_rounds(dtype, B, H, N, d, causal):
+    inp = inputs.make(B, H, N, d, dtype, seed=700 + N + d + H)
+    o, lse, _ = run_gpu(inp, causal)
+    BH = B * H
+    o = o.reshape(BH * N, d)
+    lse = lse.reshape(BH * N)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    rng = np.random.default_rng(N + H)
+    rows = np.unique(np.concatenate([
+        rng.integers(0, BH * N, size=1500),
+        [bh * N + i for bh in (0, 1, BH // 2, BH - 2, BH - 1)
+         for i in (0, 63, 64, 255, 256, N - 1) if i < N]]))
+    o_ref, lse_ref = oracle_exact(inp, causal, rows=rows)
+    assert_close(o[rows], o_ref, lse[rows], lse_ref, dtype,
+                 f"{dtype} B={B} H={H} N={N} d={d} causal={causal}")
