@@ -20,8 +20,11 @@
  *   - Tensors are contiguous row-major [B][H][N][d] (q, k, v, o) and [B][H][N]
  *     (lse), in device memory (hipMalloc / torch CUDA tensors).  Base pointers
  *     are 16-byte aligned.  Self-attention only: queries and keys share N.
- *   - The caller owns every buffer.  The library allocates no device memory,
- *     keeps no pointer after returning, and holds no mutable global state.
+ *   - The caller owns every buffer.  The library allocates no device memory
+ *     and keeps no pointer after returning.  Its only global state is a
+ *     per-device record of the compute-unit count, read on the first call
+ *     that launches on the device (the kernels run one workgroup per compute
+ *     unit, each over a list of query blocks).
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
  *     the call returns without synchronising.  A device fault surfaces at the
  *     caller's next synchronisation.
@@ -141,7 +144,7 @@ tos_status tos_attn_fwd(const void* q, const void* k, const void* v, void* o, fl
                         tos_dtype dtype, const tos_fwd_opts* opts, void* stream);
 
 /* Fills *opts with the defaults (size set, X = 32, VALU, fallback off,
- * descales 1).  Returns TOS_ERR_INVALID_ARG for NULL. */
+ * descales 1, co-scheduled).  Returns TOS_ERR_INVALID_ARG for NULL. */
 tos_status tos_fwd_opts_default(tos_fwd_opts* opts);
 
 /* Algorithmic matrix-unit work of one call: 4*B*H*N^2*d flops, halved when

@@ -2,6 +2,8 @@
 #pragma once
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 #include "attn_fwd_kernels.hpp"
 
 namespace tos {
@@ -20,15 +22,15 @@ struct KernelChoice {
 // rounded down to a multiple of 8 (the XCD count) when there are more items
 // than compute units.  The count is read once per device.
 inline int persistent_grid(int nitems) {
-  static int cus[64];
+  static std::atomic<int> cus[64];   // 0: not read yet
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = -1;
-  int n = dev >= 0 ? cus[dev] : 0;
+  int n = dev >= 0 ? cus[dev].load(std::memory_order_relaxed) : 0;
   if (n <= 0) {
     if (dev < 0 || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         n <= 0)
       n = 256;
-    if (dev >= 0) cus[dev] = n;
+    if (dev >= 0) cus[dev].store(n, std::memory_order_relaxed);
   }
   if (nitems <= n) return nitems;
   return n >= 8 ? n & ~7 : n;
