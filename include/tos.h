@@ -57,8 +57,7 @@ typedef enum {
     TOS_F32 = 0,       /* q, k, v, o: float32                                       */
     TOS_BF16 = 1,      /* q, k, v, o: bfloat16                                      */
     TOS_FP8_E4M3 = 2,  /* q, k, v: OCP float8 e4m3fn codes (x = descale * code);
-                          o: bfloat16; descales are required in the options;
-                          d = 128 only (other head dims: TOS_ERR_UNSUPPORTED)     */
+                          o: bfloat16; descales are required in the options       */
     TOS_F16 = 3        /* q, k, v, o: IEEE float16 (the same kernel family as
                           bf16, with the fp16 matrix instructions)                */
 } tos_dtype;

@@ -36,11 +36,13 @@
 // ds_read_b64_tr_b8 (per 16-lane group, lane j's byte t comes from the
 // address of lane 2t + j/8, at byte offset j%8 of it).
 //
-// LDS rows are 128 bytes (d = 128), 16-byte chunks XOR-swizzled:
-//   K: chunk c of row r at position c ^ (r & 7)
-//   V: chunk c of row r at position c ^ ((r >> 1) & 7)
-// which keeps the K operand reads (8 rows x 16 bytes per 8 lanes) and the
+// LDS rows are d bytes, 16-byte chunks XOR-swizzled (f8_kswz, f8_vswz):
+//   d = 128: K chunk c of row r at c ^ (r & 7), V at c ^ ((r >> 1) & 7)
+//   d = 64:  K chunk c of row r at c ^ ((r >> 2) & 3), V at c ^ (2 ((r >> 3) & 1))
+// which keeps the K operand reads (16 rows x 16 bytes per 16 lanes) and the
 // transposing V reads (16 rows x 32 bytes per instruction) conflict-free.
+// At d = 128 every wave loads 1 KiB of K and 1 KiB of V per step; at d = 64 a
+// block is 4 KiB, so waves 0-3 load K and waves 4-7 load V, 1 KiB each.
 #pragma once
 #include "attn_fwd_kernels.hpp"
 
@@ -51,20 +53,29 @@ typedef int i32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kF8PreScaleLog2 = 8;   // P~ * 2^8 is stored as e4m3
 
+template <int D> __device__ __forceinline__ int f8_kswz(int r, int c) {
+  return D == 128 ? (c ^ (r & 7)) : (c ^ ((r >> 2) & 3));
+}
+template <int D> __device__ __forceinline__ int f8_vswz(int r, int c) {
+  return D == 128 ? (c ^ ((r >> 1) & 7)) : (c ^ (2 * ((r >> 3) & 1)));
+}
+
 __device__ __forceinline__ f32x16 mfma_f8(i32x8 a, i32x8 b, f32x16 c) {
   // formats 0/0 = e4m3 for both operands, unit (2^0) block scales
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
-template <bool CAUSAL, int X, bool FB_AUTO>
+template <int D, bool CAUSAL, int X, bool FB_AUTO>
 __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_fp8(FwdArgs a) {
-  constexpr int D = 128;
+  static_assert(D == 64 || D == 128, "head dim");
   constexpr int RB = D;                       // bytes per K or V row
-  constexpr int BLK = kBc * RB;               // bytes per key block (8 KiB)
-  constexpr int CHW = BLK / 1024 / kPWaves;   // 1 KiB loads per wave per tensor (1)
+  constexpr int CPR = RB / 16;                // 16-byte chunks per row
+  constexpr int BLK = kBc * RB;               // bytes per key block (8 or 4 KiB)
+  constexpr bool SPLIT = D == 64;             // waves 0-3 load K, 4-7 load V
+  constexpr int NV_STEP = SPLIT ? 1 : 2;      // 1 KiB loads a wave issues per step
+  constexpr int NKK = D / 64;                 // k-steps of S^T = K Q^T
+  constexpr int NQK = 2 * NKK;                // QK matrix instructions per block
   constexpr int NMT = D / 32;                 // 32-row M tiles of O^T
-  constexpr int NV_STEP = 2 * CHW;
-  static_assert(CHW == 1, "one load instruction per wave and tensor");
   // Past the rings, 8 x 32 rows of bf16 O staging (one area per wave), as in
   // the 16-bit kernel: O leaves through LDS as whole rows.
   constexpr int ORB = 2 * D;                  // bytes per O row (bf16)
@@ -122,11 +133,11 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_fp8(FwdArgs a) {
   };
 
   // Q^T operand of k-step kk: lane (query ln, half hf) holds Q[qrow][64 kk + 32 hf + 0..31]
-  i32x8 qf[2];
+  i32x8 qf[NKK];
   auto load_q = [&](size_t head_, int qrow_, bool qvalid_) {
     const unsigned char* Q = (const unsigned char*)a.q + head_;
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
+    for (int kk = 0; kk < NKK; ++kk) {
       if (qvalid_) {
         const u32x4* src = (const u32x4*)(Q + (size_t)qrow_ * D + 64 * kk + 32 * hf);
         const u32x4 lo = src[0], hi = src[1];
@@ -138,17 +149,20 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_fp8(FwdArgs a) {
     }
   };
 
-  // direct-to-LDS loads: lane L of wave w fills bytes [1024 w + 16 L, +16) of
-  // the slot = row 8w + L/8, chunk position L%8, fetching the chunk that the
-  // swizzle puts there
+  // direct-to-LDS loads: lane L of the wave with share s (s = w, or w mod 4
+  // when the waves split K and V) fills bytes [1024 s + 16 L, +16) of the slot
+  // = row r = (1024 s + 16 L) / RB, chunk position p, fetching the chunk that
+  // the swizzle puts there
+  const int ws = SPLIT ? (w & 3) : w;
   unsigned kgoff[1], vgoff[1];
   {
-    const int r = 8 * w + lane / 8, p = lane % 8;
-    kgoff[0] = (unsigned)(r * RB + 16 * (p ^ (r & 7)));
-    vgoff[0] = (unsigned)(r * RB + 16 * (p ^ ((r >> 1) & 7)));
+    const int r = (1024 * ws + 16 * lane) / RB, p = lane % CPR;
+    kgoff[0] = (unsigned)(r * RB + 16 * f8_kswz<D>(r, p));
+    vgoff[0] = (unsigned)(r * RB + 16 * f8_vswz<D>(r, p));
   }
   const unsigned lds0 = (unsigned)(unsigned long long)(__attribute__((address_space(3))) char*)smem;
-  const unsigned vdst = lds0 + (unsigned)w * 1024, kdst = vdst + kRing * BLK;
+  const unsigned vdst = lds0 + (unsigned)ws * 1024, kdst = vdst + kRing * BLK;
+  const bool loads_k = !SPLIT || w < 4, loads_v = !SPLIT || w >= 4;   // wave-uniform
   // block j of the item's K (V), zeros past its end; with XING the blocks past
   // the end are the next item's first ones when those are prefetched
   auto ring_desc = [&](const u32x4& cur, const u32x4& nxt, int j) -> u32x4 {
@@ -156,25 +170,28 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_fp8(FwdArgs a) {
                        block_desc(cur, j, jend, BLK));
   };
   auto load_k = [&](int j, auto XING) {
+    if (!loads_k) return;
     if constexpr (decltype(XING)::value)
-      dma_block<CHW>(ring_desc(kdesc, kdesc_n, j), kdst + (j % kRing) * BLK, kgoff);
+      dma_block<1>(ring_desc(kdesc, kdesc_n, j), kdst + (j % kRing) * BLK, kgoff);
     else
-      dma_block<CHW>(block_desc(kdesc, j, jend, BLK), kdst + (j % kRing) * BLK, kgoff);
+      dma_block<1>(block_desc(kdesc, j, jend, BLK), kdst + (j % kRing) * BLK, kgoff);
   };
   auto load_v = [&](int j, auto XING) {
+    if (!loads_v) return;
     if constexpr (decltype(XING)::value)
-      dma_block<CHW>(ring_desc(vdesc, vdesc_n, j), vdst + (j % kRing) * BLK, vgoff);
+      dma_block<1>(ring_desc(vdesc, vdesc_n, j), vdst + (j % kRing) * BLK, vgoff);
     else
-      dma_block<CHW>(block_desc(vdesc, j, jend, BLK), vdst + (j % kRing) * BLK, vgoff);
+      dma_block<1>(block_desc(vdesc, j, jend, BLK), vdst + (j % kRing) * BLK, vgoff);
   };
 
   // K operand of tile u, k-step kk: lane (key ln, half hf) reads the 32 bytes
-  // of chunks 4kk + 2hf, +1 of row 32u + ln (the swizzle depends on ln & 7)
-  int koff[2][2];
+  // of chunks 4kk + 2hf, +1 of row 32u + ln (the swizzle depends on ln only
+  // through bits that 32u does not touch)
+  int koff[NKK][2];
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk)
+  for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
-    for (int e = 0; e < 2; ++e) koff[kk][e] = kRing * BLK + ln * RB + 16 * ((4 * kk + 2 * hf + e) ^ (ln & 7));
+    for (int e = 0; e < 2; ++e) koff[kk][e] = kRing * BLK + ln * RB + 16 * f8_kswz<D>(ln, 4 * kk + 2 * hf + e);
   // V operand of M tile mt, read c (0..3): lane L addresses row 16c + f(L) at
   // column 32 mt + g(L): f = 8(t/4) + 4h + t%4 with t = (L%16)/2, h = L/32;
   // g = 16((L/16)%2) + 8(L%2).  The swizzle of row 16c + f does not depend on c.
@@ -183,7 +200,7 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_fp8(FwdArgs a) {
     const int t = (lane % 16) / 2, f = 8 * (t / 4) + 4 * hf + t % 4;
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt)
-      voff[mt] = f * RB + 16 * ((2 * mt + (lane / 16) % 2) ^ ((f >> 1) & 7)) + 8 * (lane % 2);
+      voff[mt] = f * RB + 16 * f8_vswz<D>(f, 2 * mt + (lane / 16) % 2) + 8 * (lane % 2);
   }
 
   RowState st;
@@ -221,8 +238,11 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_fp8(FwdArgs a) {
   auto qk = [&](int slot, f32x16& s0, f32x16& s1) {
     s0 = mfma_f8(kread(slot, 0, 0), qf[0], f32x16{});
     s1 = mfma_f8(kread(slot, 1, 0), qf[0], f32x16{});
-    s0 = mfma_f8(kread(slot, 0, 1), qf[1], s0);
-    s1 = mfma_f8(kread(slot, 1, 1), qf[1], s1);
+#pragma unroll
+    for (int kk = 1; kk < NKK; ++kk) {
+      s0 = mfma_f8(kread(slot, 0, kk), qf[kk], s0);
+      s1 = mfma_f8(kread(slot, 1, kk), qf[kk], s1);
+    }
   };
   // O^T += V_j^T (hi + lo)^T, and the row sum of hi + lo (ones x (hi + lo)^T)
   auto pv = [&](int slot, const i32x8& hi, const i32x8& lo) {
@@ -352,15 +372,23 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_fp8(FwdArgs a) {
     // phase A: QK g = 2 kk + t, operands read one instruction ahead
     i32x8 kop = kread(kslot, 0, 0);
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
+    for (int g = 0; g < NQK; ++g) {
       const i32x8 av = kop;
-      if (g + 1 < 4) kop = kread(kslot, (g + 1) % 2, (g + 1) / 2);
+      if (g + 1 < NQK) kop = kread(kslot, (g + 1) % 2, (g + 1) / 2);
       f32x16& acc = (g % 2) ? n1 : n0;
       acc = mfma_f8(av, qf[g / 2], g < 2 ? f32x16{} : acc);
-      if (g == 0) { max_part(0, c0, c1); max_part(1, c0, c1); }
-      if (g == 1) { max_part(2, c0, c1); max_part(3, c0, c1); }
-      if (g == 2) { max_combine(); tile_ref(); }
-      if (g == 3) advance(alpha, nb);
+      if constexpr (NQK == 4) {
+        if (g == 0) { max_part(0, c0, c1); max_part(1, c0, c1); }
+        if (g == 1) { max_part(2, c0, c1); max_part(3, c0, c1); }
+        if (g == 2) { max_combine(); tile_ref(); }
+        if (g == 3) advance(alpha, nb);
+      } else {
+        if (g == 0) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) max_part(q, c0, c1);
+        }
+        if (g == 1) { max_combine(); tile_ref(); advance(alpha, nb); }
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
     // phase B: per M tile one V operand for the hi and the lo product
@@ -380,7 +408,15 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_fp8(FwdArgs a) {
       } else {
         lacc = mfma_f8(ones, i == 2 * NMT ? PH[nxt] : PL[nxt], lacc);
       }
-      if (i < 8) exp_unit(i, c0, c1, PH[cur], PL[cur], nb);
+      // the 8 exponential units: one per chunk at d = 128, spread over the
+      // 6 chunks at d = 64
+      if constexpr (D == 128) {
+        if (i < 8) exp_unit(i, c0, c1, PH[cur], PL[cur], nb);
+      } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          if (k * (2 * NMT + 2) / 8 == i) exp_unit(k, c0, c1, PH[cur], PL[cur], nb);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
     lexact = lexact * alpha + (pe[0] + pe[1]);
@@ -395,7 +431,7 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_fp8(FwdArgs a) {
   // cancels), lse = lse_scale * ref + ln(l_exact / 2^8).  finish() puts this
   // wave's O rows in its staging area (chunk c of row r at c xor (r mod 16));
   // flush() stores them as whole rows after the next item's prologue wait.
-  constexpr int CPR = ORB / 16;
+  constexpr int OCPR = ORB / 16;               // 16-byte chunks per O row
   char* const stg = smem + 2 * kRing * BLK + w * SB;
   __bf16* o_rows = nullptr;
   float* lse_rows = nullptr;
@@ -414,7 +450,7 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_fp8(FwdArgs a) {
         bf16x4 ov;
 #pragma unroll
         for (int u = 0; u < 4; ++u) ov[u] = (__bf16)(oacc[mt][4 * g + u] * inv);
-        *(bf16x4*)(stg + sr * ORB + 16 * ((4 * mt + g) ^ (sr % CPR)) + 8 * hf) = ov;
+        *(bf16x4*)(stg + sr * ORB + 16 * ((4 * mt + g) ^ (sr % OCPR)) + 8 * hf) = ov;
       }
     const int wq0 = q0 + 32 * w;
     o_rows = (__bf16*)a.o + head + (size_t)wq0 * D;
@@ -425,13 +461,13 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_fp8(FwdArgs a) {
     count_tiles<X, FB_AUTO>(a, st, lane, qrow);
   };
   auto flush = [&]() {
-    constexpr int RPI = 64 / CPR;
+    constexpr int RPI = 64 / OCPR;
     int L = lane;
     asm volatile("" : "+v"(L));
 #pragma unroll
     for (int k = 0; k < 32 / RPI; ++k) {
-      const int r = k * RPI + L / CPR, cc = L % CPR;
-      const u32x4 v = *(const u32x4*)(stg + r * ORB + 16 * (cc ^ (r % CPR)));
+      const int r = k * RPI + L / OCPR, cc = L % OCPR;
+      const u32x4 v = *(const u32x4*)(stg + r * ORB + 16 * (cc ^ (r % OCPR)));
       if (r < o_nrows) *(u32x4*)(o_rows + (size_t)r * D + 8 * cc) = v;
     }
     if (lse_rows != nullptr && hf == 0 && ln < o_nrows) lse_rows[ln] = lse_out;

@@ -4,26 +4,28 @@
 
 namespace tos {
 
-template <bool CAUSAL, int X, bool FB>
+template <int D, bool CAUSAL, int X, bool FB>
 static hipError_t go(const FwdArgs& a, hipStream_t s) {
   FwdArgs arg = a;
   arg.nqb = (a.N + kPBr - 1) / kPBr;
   const dim3 grid((unsigned)persistent_grid(arg.BH * arg.nqb)), block(kPThreads);
   void* params[] = {&arg};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&attn_fwd_fp8<CAUSAL, X, FB>), grid, block, params, 0, s);
+  return hipLaunchKernel(reinterpret_cast<const void*>(&attn_fwd_fp8<D, CAUSAL, X, FB>), grid, block, params, 0,
+                         s);
 }
 
-template <bool CAUSAL>
+template <int D, bool CAUSAL>
 static hipError_t by_x(const FwdArgs& a, const KernelChoice& k, hipStream_t s) {
-  if (k.x == 1) return k.fb_auto ? hipErrorNotSupported : go<CAUSAL, 1, false>(a, s);
-  if (k.x == 16) return k.fb_auto ? go<CAUSAL, 16, true>(a, s) : go<CAUSAL, 16, false>(a, s);
-  if (k.x == 32) return k.fb_auto ? go<CAUSAL, 32, true>(a, s) : go<CAUSAL, 32, false>(a, s);
+  if (k.x == 1) return k.fb_auto ? hipErrorNotSupported : go<D, CAUSAL, 1, false>(a, s);
+  if (k.x == 16) return k.fb_auto ? go<D, CAUSAL, 16, true>(a, s) : go<D, CAUSAL, 16, false>(a, s);
+  if (k.x == 32) return k.fb_auto ? go<D, CAUSAL, 32, true>(a, s) : go<D, CAUSAL, 32, false>(a, s);
   return hipErrorNotSupported;
 }
 
 hipError_t launch_fp8(const FwdArgs& a, const KernelChoice& k, hipStream_t s) {
-  if (k.d != 128) return hipErrorNotSupported;
-  return k.causal ? by_x<true>(a, k, s) : by_x<false>(a, k, s);
+  if (k.d == 128) return k.causal ? by_x<128, true>(a, k, s) : by_x<128, false>(a, k, s);
+  if (k.d == 64) return k.causal ? by_x<64, true>(a, k, s) : by_x<64, false>(a, k, s);
+  return hipErrorNotSupported;
 }
 
 }  // namespace tos

@@ -134,7 +134,6 @@ tos_status tos_attn_fwd(const void* q, const void* k, const void* v, void* o, fl
   if (kc.seq && ((dtype != TOS_BF16 && dtype != TOS_F16) || kc.rowsum_mfma || kc.fb_auto ||
                  kc.x == 16))
     return TOS_ERR_UNSUPPORTED;
-  if (dtype == TOS_FP8_E4M3 && d != 128) return TOS_ERR_UNSUPPORTED;
 
   tos::FwdArgs a;
   a.q = q;

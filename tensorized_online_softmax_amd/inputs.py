@@ -137,13 +137,11 @@ def grid_workload(N, d, dtype, causal, x_tile=32, seed=6000):
 
 
 def grid(dtypes=("bf16", "f16", "fp8"), causal=(False, True)):
-    """Every point of the page's grid that the library supports (fp8: d = 128)."""
+    """Every point of the page's grid, for the given dtypes."""
     out = []
     for dt in dtypes:
         for c in causal:
             for d in GRID_D:
-                if dt == "fp8" and d != 128:
-                    continue
                 for n in GRID_N:
                     out.append(grid_workload(n, d, dt, c))
     return out

@@ -93,7 +93,7 @@ def opts(**kw):
     (dict(dtype=tb.TOS_FP8_E4M3, opts=opts(q_descale=0.0)), tb.TOS_ERR_INVALID_ARG),
     (dict(dtype=tb.TOS_FP8_E4M3, opts=opts(v_descale=float("nan"))), tb.TOS_ERR_INVALID_ARG),
     (dict(dtype=tb.TOS_F32, opts=opts(softmax_split=1)), tb.TOS_ERR_UNSUPPORTED),
-    (dict(dtype=tb.TOS_FP8_E4M3, d=64), tb.TOS_ERR_UNSUPPORTED),   # fp8: d = 128 only
+    (dict(dtype=tb.TOS_FP8_E4M3, d=96), tb.TOS_ERR_UNSUPPORTED),
     (dict(dtype=tb.TOS_F16, d=96), tb.TOS_ERR_UNSUPPORTED),
     (dict(opts=opts(schedule=2)), tb.TOS_ERR_INVALID_ARG),
     # the sequential schedule: 16-bit inputs, VALU row sum, no AUTO, X = 1 or 32

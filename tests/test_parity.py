@@ -144,7 +144,7 @@ def test_one_hot_v_rows_sum_to_one():
             assert np.all(np.triu(o, 1) == 0.0)
 
 
-# ---- fp8 e4m3 (d = 128), against exact attention on the decoded inputs
+# ---- fp8 e4m3 (d = 64 and 128), against exact attention on the decoded inputs
 #
 # The P~V product takes P~ as two e4m3 terms (hi + lo): with one e4m3 rounding
 # of P~ the oracle's fp64 model of the method itself misses the 6e-2 bound on
@@ -159,20 +159,22 @@ def _fp8_check(inp, causal, x_tile=32, fallback="off", tau=0.0, what=""):
     return tiles
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("N", SMALL_N)
-def test_fp8_small_full(causal, N):
-    inp = _inp(2, 3, N, 128, "fp8", seed=300 + N)
-    _fp8_check(inp, causal, what=f"fp8 causal={causal} N={N}")
+def test_fp8_small_full(d, causal, N):
+    inp = _inp(2, 3, N, d, "fp8", seed=300 + N + d)
+    _fp8_check(inp, causal, what=f"fp8 d={d} causal={causal} N={N}")
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("x_tile", [1, 16, 32])
 @pytest.mark.parametrize("fallback", ["off", "auto", "force"])
 @pytest.mark.parametrize("causal", [False, True])
-def test_fp8_knobs(x_tile, fallback, causal):
+def test_fp8_knobs(d, x_tile, fallback, causal):
     if x_tile == 1 and fallback == "auto":
         pytest.skip("AUTO needs a tile of more than one row")
-    inp = _inp(1, 4, 300, 128, "fp8", seed=17)
+    inp = _inp(1, 4, 300, d, "fp8", seed=17 + d)
     tiles = _fp8_check(inp, causal, x_tile=x_tile, fallback=fallback,
                        what=f"fp8 X={x_tile} fallback={fallback} causal={causal}")
     if fallback == "force":
@@ -259,6 +261,8 @@ def test_grid_sampled(w):
     ("f16", 2, 150, 700, 64),
     ("fp8", 1, 300, 300, 128),
     ("fp8", 2, 160, 520, 128),
+    ("fp8", 1, 300, 300, 64),
+    ("fp8", 2, 150, 1000, 64),
 ])
 @pytest.mark.parametrize("causal", [False, True])
 def test_persistent_rounds(dtype, B, H, N, d, causal):
