@@ -198,6 +198,7 @@ ABLATION = [
     ("tile16_cosched", 16, "valu", "cosched"),           # Max16 analog
     ("tile32_sequential", 32, "valu", "sequential"),
     ("tile32_cosched", 32, "valu", "cosched"),           # FA-T analog (the default)
+    ("tile64_cosched", 64, "valu", "cosched"),           # tiles of two waves
     ("tile32_rowsum_mfma", 32, "rowsum_mfma", "cosched"),
 ]
 

@@ -102,8 +102,11 @@ typedef enum {
 
 typedef struct {
     int size;              /* sizeof(tos_fwd_opts): the struct version             */
-    int x_tile;            /* surrogate tile rows X: 0 = default (32), 1, 16 or 32;
-                              X = 1 is the per-row online softmax                  */
+    int x_tile;            /* surrogate tile rows X: 0 = default (32), 1, 16, 32 or
+                              64; X = 1 is the per-row online softmax; X = 64 (two
+                              waves exchange their halves through LDS) needs
+                              bf16/f16 and the VALU row sum, else
+                              TOS_ERR_UNSUPPORTED                                  */
     int softmax_split;     /* a tos_softmax_split value                             */
     int fallback;          /* a tos_fallback value                                  */
     float fallback_tau;    /* AUTO threshold in log2 units; 0 = default (100 for

@@ -129,7 +129,7 @@ __device__ __forceinline__ void count_tiles(const FwdArgs& a, const RowState& st
                                             int qrow) {
   if (a.fallback_tiles == nullptr || lane >= 32 || qrow >= a.N) return;
   if constexpr (FB_AUTO) {
-    if (st.per_row && (lane % X) == 0) atomicAdd(a.fallback_tiles, 1);
+    if (st.per_row && (qrow % X) == 0) atomicAdd(a.fallback_tiles, 1);
   } else {
     if (a.count_x > 0 && (qrow % a.count_x) == 0) atomicAdd(a.fallback_tiles, 1);
   }
@@ -325,8 +325,11 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_h16(FwdArgs a) {
     kdesc = buffer_desc((const E*)a.k + head, (unsigned)N * RB);
     vdesc = buffer_desc((const E*)a.v + head, (unsigned)N * RB);
     jend = item_jend(q0);
-    const int wq0 = q0 + 32 * w;                       // first query of the wave
-    jend_w = (wq0 >= N) ? 0 : (CAUSAL ? min(wq0 + 31, N - 1) / kBc + 1 : nblk);
+    // first query of the wave (X = 64: of its pair of waves, which must step
+    // through the same key blocks to exchange their tile maxima)
+    const int wq0 = X == 64 ? q0 + 64 * (w / 2) : q0 + 32 * w;
+    const int wrows = X == 64 ? 64 : 32;
+    jend_w = (wq0 >= N) ? 0 : (CAUSAL ? min(wq0 + wrows - 1, N - 1) / kBc + 1 : nblk);
     klim = qvalid ? (CAUSAL ? qrow + 1 : N) : 0;       // keys this lane may see
   };
   // The next item's first K and V blocks are loaded by this item's last steps
@@ -501,7 +504,44 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_h16(FwdArgs a) {
   // the tile maximum (the surrogate) and the new reference: alpha, and
   // -c * ref for the exponentials
   float ref_new = 0.0f;
-  auto tile_ref = [&]() { ref_new = block_ref<X, FB_AUTO>(st, c, tau); };
+  // X = 64: the tile is waves 2p and 2p+1.  Each publishes the maximum (and,
+  // with AUTO, the minimum) of its 32 rows' running maxima in LDS under a
+  // per-block sequence number and takes its partner's; the partner cannot be a
+  // block ahead (the step barrier), so the slot holds this block's value or
+  // the last one.  The wait is bounded: past it the wave keeps its own half
+  // (any reference at least the rows' maxima gives the same result).  The
+  // slots are the last 128 bytes of wave 7's O staging area, which that wave's
+  // row 31 bypasses.
+  float* const xslot = (float*)(smem + 2 * kRing * BLK + 4 * (32 * RB) - 128);
+  int xseq = 0;
+  auto tile_ref = [&]() {
+    if constexpr (X == 64) {
+      const float ninf = -__builtin_inff();
+      const float own = tile_reduce<32>(st.m_run, MaxOp());
+      const float own_mn = FB_AUTO ? tile_reduce<32>(st.m_run == ninf ? __builtin_inff() : st.m_run, MinOp())
+                                   : 0.0f;
+      ++xseq;
+      float* mine = xslot + 4 * w;
+      if (lane == 0) {
+        mine[0] = own;
+        mine[1] = own_mn;
+        __hip_atomic_store((int*)(mine + 2), xseq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+      }
+      const float* other = xslot + 4 * (w ^ 1);
+      float pmx = own, pmn = own_mn;
+      int tries = 0;
+      while (__hip_atomic_load((const int*)(other + 2), __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) != xseq &&
+             ++tries < (1 << 16))
+        __builtin_amdgcn_s_sleep(1);
+      if (tries < (1 << 16)) {
+        pmx = other[0];
+        pmn = other[1];
+      }
+      ref_new = ref_from_tile<FB_AUTO>(st, fmax_raw(own, pmx), fmin_raw(own_mn, pmn), c, tau);
+    } else {
+      ref_new = block_ref<X, FB_AUTO>(st, c, tau);
+    }
+  };
   auto advance = [&](float& alpha, float& nb) {
     alpha = ref_advance(st, ref_new, c);
     nb = neg_c_ref(st, c) + (float)Elem16<E>::kPreLog2;
@@ -683,6 +723,9 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_h16(FwdArgs a) {
     // hoisted out of the item loop to hold registers through it)
     int sr = ln;
     asm volatile("" : "+v"(sr));
+    // (X = 64: wave 7's row 31 goes straight to memory; its staging bytes hold
+    // the tile-maximum exchange)
+    const bool direct = X == 64 && w == 7 && ln == 31;
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
@@ -690,7 +733,10 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_h16(FwdArgs a) {
         ev4 ov;
 #pragma unroll
         for (int u = 0; u < 4; ++u) ov[u] = (E)(oacc[mt][4 * g + u] * inv);
-        *(ev4*)(stg + sr * RB + 16 * ((4 * mt + g) ^ (sr % CPR)) + 8 * hf) = ov;
+        if (!direct)
+          *(ev4*)(stg + sr * RB + 16 * ((4 * mt + g) ^ (sr % CPR)) + 8 * hf) = ov;
+        else if (qvalid)
+          *(ev4*)((E*)a.o + head + (size_t)qrow * D + 32 * mt + 8 * g + 4 * hf) = ov;
       }
     const int wq0 = q0 + 32 * w;
     o_rows = (E*)a.o + head + (size_t)wq0 * D;
@@ -708,11 +754,14 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_h16(FwdArgs a) {
     for (int k = 0; k < 32 / RPI; ++k) {
       const int r = k * RPI + L / CPR, cc = L % CPR;
       const ev8 v = *(const ev8*)(stg + r * RB + 16 * (cc ^ (r % CPR)));
-      if (r < o_nrows) *(ev8*)(o_rows + (size_t)r * D + 8 * cc) = v;
+      if (r < o_nrows && !(X == 64 && w == 7 && r == 31)) *(ev8*)(o_rows + (size_t)r * D + 8 * cc) = v;
     }
     if (lse_rows != nullptr && hf == 0 && ln < o_nrows) lse_rows[ln] = lse_out;
   };
 
+  if constexpr (X == 64) {   // sequence numbers start at 1: clear them (the
+    if (lane == 0) ((int*)xslot)[4 * w + 2] = 0;   // first barrier publishes it)
+  }
   int it = item_of(0, gid, nwg);
   set_item(it);
   bool pref = false;   // this item's first blocks are in the rings already

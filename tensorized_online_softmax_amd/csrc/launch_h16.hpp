@@ -34,6 +34,10 @@ static hipError_t by_x_h16(const FwdArgs& a, const KernelChoice& k, hipStream_t 
       return k.fb_auto ? go_h16<E, D, CAUSAL, 16, true, true>(a, s) : go_h16<E, D, CAUSAL, 16, true, false>(a, s);
     return k.fb_auto ? go_h16<E, D, CAUSAL, 16, false, true>(a, s) : go_h16<E, D, CAUSAL, 16, false, false>(a, s);
   }
+  if (k.x == 64) {   // tiles of two waves: VALU row sum only
+    if (k.rowsum_mfma) return hipErrorNotSupported;
+    return k.fb_auto ? go_h16<E, D, CAUSAL, 64, false, true>(a, s) : go_h16<E, D, CAUSAL, 64, false, false>(a, s);
+  }
   if (k.x == 32) {
     if (k.rowsum_mfma)
       return k.fb_auto ? go_h16<E, D, CAUSAL, 32, true, true>(a, s) : go_h16<E, D, CAUSAL, 32, true, false>(a, s);

@@ -4,7 +4,8 @@
 // lane L of a 64-wide wave owns query (L mod 32) of the wave's 32 queries; lanes
 // L and L+32 hold different keys of the same query.  So a row's statistics are
 // combined across the lane pair (L, L+32), and an X-row tile (X = 16 or 32) is a
-// set of X consecutive lanes mod 32.
+// set of X consecutive lanes mod 32.  (X = 64 spans two waves; the kernels
+// combine the two 32-row halves.)
 //
 // The surrogate maximum (FlashAttention-T, section A2, "surrogate maximum"): the
 // reference subtracted from a row's logits is the largest running row maximum
@@ -101,6 +102,18 @@ __device__ __forceinline__ float block_ref(RowState& st, float c, float tau) {
     } else {
       return tm;
     }
+  }
+}
+
+// The same reference from a tile's maximum tm and minimum mn of the running row
+// maxima (rows without a key left out of mn), for tiles that span two waves.
+template <bool FB_AUTO>
+__device__ __forceinline__ float ref_from_tile(RowState& st, float tm, float mn, float c, float tau) {
+  if constexpr (FB_AUTO) {
+    st.per_row = st.per_row || (c * (tm - mn) > tau);
+    return st.per_row ? st.m_run : tm;
+  } else {
+    return tm;
   }
 }
 

@@ -79,7 +79,8 @@ tos_status tos_attn_fwd(const void* q, const void* k, const void* v, void* o, fl
     op = *opts;
     if (op.x_tile == 0) op.x_tile = 32;
   }
-  if (op.x_tile != 1 && op.x_tile != 16 && op.x_tile != 32) return TOS_ERR_INVALID_ARG;
+  if (op.x_tile != 1 && op.x_tile != 16 && op.x_tile != 32 && op.x_tile != 64)
+    return TOS_ERR_INVALID_ARG;
   if (op.softmax_split != TOS_SPLIT_VALU && op.softmax_split != TOS_SPLIT_ROWSUM_MFMA)
     return TOS_ERR_INVALID_ARG;
   if (op.fallback != TOS_FALLBACK_OFF && op.fallback != TOS_FALLBACK_AUTO &&
@@ -132,7 +133,10 @@ tos_status tos_attn_fwd(const void* q, const void* k, const void* v, void* o, fl
   kc.seq = op.schedule == TOS_SCHEDULE_SEQUENTIAL;
   if (dtype == TOS_F32 && kc.rowsum_mfma) return TOS_ERR_UNSUPPORTED;
   if (kc.seq && ((dtype != TOS_BF16 && dtype != TOS_F16) || kc.rowsum_mfma || kc.fb_auto ||
-                 kc.x == 16))
+                 kc.x == 16 || kc.x == 64))
+    return TOS_ERR_UNSUPPORTED;
+  // X = 64 (tiles of two waves): the 16-bit kernels with the VALU row sum
+  if (kc.x == 64 && ((dtype != TOS_BF16 && dtype != TOS_F16) || kc.rowsum_mfma))
     return TOS_ERR_UNSUPPORTED;
 
   tos::FwdArgs a;

@@ -86,7 +86,11 @@ def opts(**kw):
     (dict(d=256), tb.TOS_ERR_UNSUPPORTED),
     (dict(opts=opts(size=4)), tb.TOS_ERR_INVALID_ARG),
     (dict(opts=opts(x_tile=8)), tb.TOS_ERR_INVALID_ARG),
-    (dict(opts=opts(x_tile=64)), tb.TOS_ERR_INVALID_ARG),
+    (dict(opts=opts(x_tile=128)), tb.TOS_ERR_INVALID_ARG),
+    (dict(dtype=tb.TOS_F32, opts=opts(x_tile=64)), tb.TOS_ERR_UNSUPPORTED),
+    (dict(dtype=tb.TOS_FP8_E4M3, opts=opts(x_tile=64)), tb.TOS_ERR_UNSUPPORTED),
+    (dict(opts=opts(x_tile=64, softmax_split=1)), tb.TOS_ERR_UNSUPPORTED),
+    (dict(opts=opts(x_tile=64, schedule=1)), tb.TOS_ERR_UNSUPPORTED),
     (dict(opts=opts(softmax_split=5)), tb.TOS_ERR_INVALID_ARG),
     (dict(opts=opts(fallback=3)), tb.TOS_ERR_INVALID_ARG),
     (dict(opts=opts(fallback_tau=-1.0)), tb.TOS_ERR_INVALID_ARG),

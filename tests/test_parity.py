@@ -41,13 +41,15 @@ def test_small_full(dtype, d, causal, N):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
-@pytest.mark.parametrize("x_tile", [1, 16, 32])
+@pytest.mark.parametrize("x_tile", [1, 16, 32, 64])
 @pytest.mark.parametrize("split", ["valu", "rowsum_mfma"])
 @pytest.mark.parametrize("fallback", ["off", "auto", "force"])
 @pytest.mark.parametrize("causal", [False, True])
 def test_knobs(dtype, x_tile, split, fallback, causal):
     if dtype == "f32" and split == "rowsum_mfma":
         pytest.skip("row sum on the matrix unit is a 16-bit option")
+    if x_tile == 64 and fallback != "force" and (dtype == "f32" or split == "rowsum_mfma"):
+        pytest.skip("X = 64 runs in the 16-bit kernels with the vector row sum")
     inp = _inp(1, 4, 300, 64, dtype, seed=7)
     o_ref, lse_ref = oracle_exact(inp, causal)
     o, lse, tiles = run_gpu(inp, causal, x_tile=x_tile, split=split, fallback=fallback,
@@ -280,3 +282,47 @@ def test_persistent_rounds(dtype, B, H, N, d, causal):
     o_ref, lse_ref = oracle_exact(inp, causal, rows=rows)
     assert_close(o[rows], o_ref, lse[rows], lse_ref, dtype,
                  f"{dtype} B={B} H={H} N={N} d={d} causal={causal}")
+
+
+@pytest.mark.parametrize("dtype,B,H,N,d", [
+    ("bf16", 1, 300, 300, 128),
+    ("bf16", 2, 160, 520, 64),
+    ("f16", 1, 130, 1000, 128),
+])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("fallback", ["off", "auto"])
+def test_x64_tiles(dtype, B, H, N, d, causal, fallback):
+    """X = 64 (two waves exchange their halves of the tile maximum through
+    LDS), with several items per workgroup and ragged last query blocks."""
+    inp = inputs.make(B, H, N, d, dtype, seed=900 + N + d + H)
+    o, lse, tiles = run_gpu(inp, causal, x_tile=64, fallback=fallback, counter=True)
+    assert tiles == 0
+    BH = B * H
+    o = o.reshape(BH * N, d)
+    lse = lse.reshape(BH * N)
+    rng = np.random.default_rng(N + H + d)
+    rows = np.unique(np.concatenate([
+        rng.integers(0, BH * N, size=1200),
+        [bh * N + i for bh in (0, 1, BH - 1) for i in (0, 31, 32, 63, 64, 255, N - 1) if i < N]]))
+    o_ref, lse_ref = oracle_exact(inp, causal, rows=rows)
+    assert_close(o[rows], o_ref, lse[rows], lse_ref, dtype,
+                 f"X=64 {dtype} B={B} H={H} N={N} d={d} causal={causal} fallback={fallback}")
+
+
+def test_x64_fallback_counts_tiles():
+    """Spiky rows with a low AUTO threshold: X = 64 switches 64-row tiles, and
+    the count matches the oracle's recurrence at X = 64 on the same inputs."""
+    N, d = 512, 128
+    inp = inputs.make(1, 2, N, d, "bf16", seed=58, std=math.sqrt(8.0), spike_frac=0.2,
+                      spike_logit=40.0)
+    o_ref, lse_ref = oracle_exact(inp, False)
+    o, lse, tiles = run_gpu(inp, False, x_tile=64, fallback="auto", tau=12.0, counter=True)
+    assert_close(o.reshape(o_ref.shape), o_ref, lse.reshape(lse_ref.shape), lse_ref, "bf16",
+                 "X=64 spiky AUTO", storage_ulp=True)
+    q, k, v = real_inputs(inp)
+    model = oracle.attn_surrogate(q, k, v, False, inp["scale"], X=64, Bc=64, fallback=1,
+                                  tau=12.0)
+    want = int(model["switched"].sum())
+    # (the switch compares a gap with tau in fp32 in the kernel and fp64 in the
+    # oracle: a gap within rounding of tau could fall either way)
+    assert want > 0 and abs(tiles - want) <= 1, (tiles, want)
