@@ -190,8 +190,9 @@ def grid_sweep(dtypes, steps, warmup):
 
 # The ablation's knob settings, after FlashAttention-T's evaluation (section
 # A4, Fig 9 and Fig 10: FA2, FA2 + Max16, AllTensor, FA-T): name, X, row-sum
-# split, schedule.  The pages' AllTensor (scaling and FMA on the tensor unit)
-# has no counterpart here: gfx950 has no TF32 matrix instruction.
+# split, schedule.  The pages' AllTensor puts scaling and FMA on the tensor
+# unit; gfx950 has no TF32 matrix instruction, and the setting here scales O
+# with fp32 products (the FMA before exp2 stays a vector instruction).
 ABLATION = [
     ("per_row_sequential", 1, "valu", "sequential"),     # FA2 analog
     ("per_row_cosched", 1, "valu", "cosched"),
@@ -200,6 +201,7 @@ ABLATION = [
     ("tile32_cosched", 32, "valu", "cosched"),           # FA-T analog (the default)
     ("tile64_cosched", 64, "valu", "cosched"),           # tiles of two waves
     ("tile32_rowsum_mfma", 32, "rowsum_mfma", "cosched"),
+    ("tile32_scale_mfma", 32, "scale_mfma", "cosched"),  # O rescale on the matrix unit
 ]
 
 
@@ -255,7 +257,7 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="causal_bf16")
-    ap.add_argument("--split", default="valu", choices=["valu", "rowsum_mfma"])
+    ap.add_argument("--split", default="valu", choices=["valu", "rowsum_mfma", "scale_mfma"])
     ap.add_argument("--schedule", default="cosched", choices=["cosched", "sequential"],
                     help="sequential: the no-co-scheduling ablation (16-bit inputs)")
     ap.add_argument("--ablation", action="store_true",

@@ -67,8 +67,13 @@ typedef enum {
 typedef enum {
     TOS_SPLIT_VALU = 0,         /* vector-unit dot products of the packed P~ pairs
                                    with (1, 1)                                      */
-    TOS_SPLIT_ROWSUM_MFMA = 1   /* matrix-unit contraction of the packed P~ against a
+    TOS_SPLIT_ROWSUM_MFMA = 1,  /* matrix-unit contraction of the packed P~ against a
                                    constant all-ones operand (bf16, f16; not fp32)  */
+    TOS_SPLIT_SCALE_MFMA = 2    /* VALU row sum, and the O rescale by the tile's
+                                   factor on the matrix unit (section A2, Fig 5(a):
+                                   fp32 products against alpha I).  An A/B variant:
+                                   bf16/f16, X = 32, fallback off, co-scheduled
+                                   only (else TOS_ERR_UNSUPPORTED)                  */
 } tos_softmax_split;
 /* Either way l sums the rounded P~ that the P~V product consumes, and a separate
  * unrounded fp32 sum gives lse.  TOS_FP8_E4M3 has no vector form for e4m3

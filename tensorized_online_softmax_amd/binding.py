@@ -13,7 +13,7 @@ LIB_PATH = os.path.join(_PKG, "libtos.so")
 
 TOS_OK, TOS_ERR_INVALID_ARG, TOS_ERR_UNSUPPORTED, TOS_ERR_HIP = 0, 1, 2, 3
 TOS_F32, TOS_BF16, TOS_FP8_E4M3, TOS_F16 = 0, 1, 2, 3
-TOS_SPLIT_VALU, TOS_SPLIT_ROWSUM_MFMA = 0, 1
+TOS_SPLIT_VALU, TOS_SPLIT_ROWSUM_MFMA, TOS_SPLIT_SCALE_MFMA = 0, 1, 2
 TOS_FALLBACK_OFF, TOS_FALLBACK_AUTO, TOS_FALLBACK_FORCE = 0, 1, 2
 TOS_SCHEDULE_COSCHED, TOS_SCHEDULE_SEQUENTIAL = 0, 1
 
@@ -111,7 +111,8 @@ def tos_version():
 
 
 _DTYPE_CODES = {"f32": TOS_F32, "bf16": TOS_BF16, "fp8": TOS_FP8_E4M3, "f16": TOS_F16}
-_SPLITS = {"valu": TOS_SPLIT_VALU, "rowsum_mfma": TOS_SPLIT_ROWSUM_MFMA}
+_SPLITS = {"valu": TOS_SPLIT_VALU, "rowsum_mfma": TOS_SPLIT_ROWSUM_MFMA,
+           "scale_mfma": TOS_SPLIT_SCALE_MFMA}
 _FALLBACKS = {"off": TOS_FALLBACK_OFF, "auto": TOS_FALLBACK_AUTO, "force": TOS_FALLBACK_FORCE}
 _SCHEDULES = {"cosched": TOS_SCHEDULE_COSCHED, "sequential": TOS_SCHEDULE_SEQUENTIAL}
 

@@ -276,7 +276,9 @@ template <int I> struct Int { static constexpr int value = I; };
 
 // SEQ: the sequential-schedule ablation -- every step is the generic step
 // (softmax, then QK^T, then P~V), with no interleaving inside a wave.
-template <typename E, int D, bool CAUSAL, int X, bool ROWSUM_MFMA, bool FB_AUTO, bool SEQ>
+// SCALE_MFMA: the O rescale on the matrix unit (an A/B variant, X = 32 only).
+template <typename E, int D, bool CAUSAL, int X, bool ROWSUM_MFMA, bool FB_AUTO, bool SEQ,
+          bool SCALE_MFMA = false>
 __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_h16(FwdArgs a) {
   typedef typename Elem16<E>::v8 ev8;
   typedef typename Elem16<E>::v4 ev4;
@@ -578,8 +580,29 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_h16(FwdArgs a) {
   // reference moved (alpha == 1 everywhere, the common case)
   auto rescale = [&](float alpha) {
     if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+      if constexpr (SCALE_MFMA) {
+        // The repurposed-MMA scaling of FlashAttention-T (section A2, Fig 5(a))
+        // in fp32: O^T <- (alpha I) O^T as sixteen 32x32x2 f32 products per
+        // 32x32 tile.  Slice s pairs accumulator register s of the two lane
+        // halves (rows 8(s/4) + 4h + s%4, h = 0, 1) as the B operand with the
+        // matching columns of alpha I as the A operand.  alpha is the same in
+        // every lane here (one X = 32 tile per wave, no per-row fallback).
+        const int m = lane & 31, h = lane >> 5;
 #pragma unroll
-      for (int mt = 0; mt < NMT; ++mt) oacc[mt] *= alpha;
+        for (int mt = 0; mt < NMT; ++mt) {
+          f32x16 dacc = {};
+#pragma unroll
+          for (int sl = 0; sl < 16; ++sl) {
+            const float av = (m == 8 * (sl / 4) + 4 * h + sl % 4) ? alpha : 0.0f;
+            dacc = __builtin_amdgcn_mfma_f32_32x32x2f32(av, oacc[mt][sl], dacc, 0, 0, 0);
+          }
+          oacc[mt] = dacc;
+          __builtin_amdgcn_sched_barrier(0);   // one tile's products at a time
+        }
+      } else {
+#pragma unroll
+        for (int mt = 0; mt < NMT; ++mt) oacc[mt] *= alpha;
+      }
       if constexpr (ROWSUM_MFMA) lacc *= alpha;
     }
   };

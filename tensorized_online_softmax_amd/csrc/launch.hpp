@@ -15,6 +15,7 @@ struct KernelChoice {
   bool rowsum_mfma;  // row sum on the matrix unit (fp8: always)
   bool fb_auto;      // fallback AUTO (x > 1 only)
   bool seq = false;  // sequential schedule (16-bit kernels, x = 1 or 32, VALU row sum, no AUTO)
+  bool scale_mfma = false;   // O rescale on the matrix unit (16-bit kernels, x = 32, no fallback)
 };
 
 // Workgroups of a persistent launch over `nitems` items: one per compute unit

@@ -5,7 +5,7 @@
 
 namespace tos {
 
-template <typename E, int D, bool CAUSAL, int X, bool RS, bool FB, bool SEQ = false>
+template <typename E, int D, bool CAUSAL, int X, bool RS, bool FB, bool SEQ = false, bool SCALE = false>
 static hipError_t go_h16(const FwdArgs& a, hipStream_t s) {
   FwdArgs arg = a;
   arg.nqb = (a.N + kPBr - 1) / kPBr;
@@ -13,12 +13,16 @@ static hipError_t go_h16(const FwdArgs& a, hipStream_t s) {
   // hipLaunchKernel reports this launch's own status (hipGetLastError could
   // return an error left behind by an earlier, unrelated call)
   void* params[] = {&arg};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&attn_fwd_h16<E, D, CAUSAL, X, RS, FB, SEQ>), grid,
+  return hipLaunchKernel(reinterpret_cast<const void*>(&attn_fwd_h16<E, D, CAUSAL, X, RS, FB, SEQ, SCALE>), grid,
                          block, params, 0, s);
 }
 
 template <typename E, int D, bool CAUSAL>
 static hipError_t by_x_h16(const FwdArgs& a, const KernelChoice& k, hipStream_t s) {
+  if (k.scale_mfma) {   // the O rescale on the matrix unit: X = 32, VALU row sum, no AUTO
+    if (k.x != 32 || k.rowsum_mfma || k.fb_auto || k.seq) return hipErrorNotSupported;
+    return go_h16<E, D, CAUSAL, 32, false, false, false, true>(a, s);
+  }
   if (k.seq) {   // the sequential-schedule ablation: VALU row sum, no AUTO
     if (k.rowsum_mfma || k.fb_auto) return hipErrorNotSupported;
     if (k.x == 1) return go_h16<E, D, CAUSAL, 1, false, false, true>(a, s);

@@ -81,7 +81,8 @@ tos_status tos_attn_fwd(const void* q, const void* k, const void* v, void* o, fl
   }
   if (op.x_tile != 1 && op.x_tile != 16 && op.x_tile != 32 && op.x_tile != 64)
     return TOS_ERR_INVALID_ARG;
-  if (op.softmax_split != TOS_SPLIT_VALU && op.softmax_split != TOS_SPLIT_ROWSUM_MFMA)
+  if (op.softmax_split != TOS_SPLIT_VALU && op.softmax_split != TOS_SPLIT_ROWSUM_MFMA &&
+      op.softmax_split != TOS_SPLIT_SCALE_MFMA)
     return TOS_ERR_INVALID_ARG;
   if (op.fallback != TOS_FALLBACK_OFF && op.fallback != TOS_FALLBACK_AUTO &&
       op.fallback != TOS_FALLBACK_FORCE)
@@ -131,6 +132,12 @@ tos_status tos_attn_fwd(const void* q, const void* k, const void* v, void* o, fl
   kc.x = op.fallback == TOS_FALLBACK_FORCE ? 1 : op.x_tile;
   kc.fb_auto = op.fallback == TOS_FALLBACK_AUTO && op.x_tile > 1;
   kc.seq = op.schedule == TOS_SCHEDULE_SEQUENTIAL;
+  kc.scale_mfma = op.softmax_split == TOS_SPLIT_SCALE_MFMA;
+  // the O rescale on the matrix unit needs one uniform factor per wave: an
+  // X = 32 tile and no fallback, in the 16-bit kernels
+  if (kc.scale_mfma && ((dtype != TOS_BF16 && dtype != TOS_F16) || op.x_tile != 32 ||
+                        op.fallback != TOS_FALLBACK_OFF || kc.seq))
+    return TOS_ERR_UNSUPPORTED;
   if (dtype == TOS_F32 && kc.rowsum_mfma) return TOS_ERR_UNSUPPORTED;
   if (kc.seq && ((dtype != TOS_BF16 && dtype != TOS_F16) || kc.rowsum_mfma || kc.fb_auto ||
                  kc.x == 16 || kc.x == 64))

@@ -92,6 +92,11 @@ def opts(**kw):
     (dict(opts=opts(x_tile=64, softmax_split=1)), tb.TOS_ERR_UNSUPPORTED),
     (dict(opts=opts(x_tile=64, schedule=1)), tb.TOS_ERR_UNSUPPORTED),
     (dict(opts=opts(softmax_split=5)), tb.TOS_ERR_INVALID_ARG),
+    (dict(dtype=tb.TOS_F32, opts=opts(softmax_split=2)), tb.TOS_ERR_UNSUPPORTED),
+    (dict(dtype=tb.TOS_FP8_E4M3, opts=opts(softmax_split=2)), tb.TOS_ERR_UNSUPPORTED),
+    (dict(opts=opts(softmax_split=2, x_tile=16)), tb.TOS_ERR_UNSUPPORTED),
+    (dict(opts=opts(softmax_split=2, fallback=1)), tb.TOS_ERR_UNSUPPORTED),
+    (dict(opts=opts(softmax_split=2, schedule=1)), tb.TOS_ERR_UNSUPPORTED),
     (dict(opts=opts(fallback=3)), tb.TOS_ERR_INVALID_ARG),
     (dict(opts=opts(fallback_tau=-1.0)), tb.TOS_ERR_INVALID_ARG),
     (dict(dtype=tb.TOS_FP8_E4M3, opts=opts(q_descale=0.0)), tb.TOS_ERR_INVALID_ARG),

@@ -82,6 +82,20 @@ def test_sequential_schedule(dtype, d, x_tile, causal, N):
                  f"sequential {dtype} d={d} X={x_tile} causal={causal} N={N}")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [100, 520, 1024])
+def test_scale_on_matrix_unit(dtype, d, causal, N):
+    """The O rescale on the matrix unit (f32 products against alpha I) computes
+    the same attention."""
+    inp = _inp(2, 2, N, d, dtype, seed=400 + N + d)
+    o_ref, lse_ref = oracle_exact(inp, causal)
+    o, lse, _ = run_gpu(inp, causal, split="scale_mfma")
+    assert_close(o.reshape(o_ref.shape), o_ref, lse.reshape(lse_ref.shape), lse_ref, dtype,
+                 f"scale_mfma {dtype} d={d} causal={causal} N={N}")
+
+
 def test_fallback_auto_switches_on_spiky_rows():
     """Spiky rows next to flat rows with a low threshold: AUTO switches tiles to
     per-row maxima and still matches; OFF and AUTO agree with the oracle."""
