@@ -153,9 +153,16 @@ __device__ __forceinline__ void count_tiles(const FwdArgs& a, const RowState& st
 // Key blocks stream into two LDS rings of 4 slots (K and V) through buffer
 // loads that write LDS directly (no registers; rows past N read as 0).  Step j
 // issues K_{j+4} and V_{j+2} into the slots that K_j and V_{j-2} held (read in
-// step j-1); blocks at or past the workgroup's last one are fetched as zeros,
-// so every step issues the same loads.  Every step ends with a plain barrier
-// after waiting until only the loads of the last two steps are in flight.
+// step j-1); blocks past an item's last one are the next item's first ones
+// (see below) or zeros, so every step issues the same loads.  Every step ends
+// with a plain barrier after waiting until only the loads of the last two
+// steps are in flight.
+//
+// The launch is persistent: one workgroup per compute unit, each running a
+// static list of items (256-row query blocks of a head, heaviest first, see
+// item_of).  The rings run on across items, the next item's Q is loaded in
+// the last step of the current one, and O leaves through LDS as whole rows
+// after the next item's prologue wait.
 // A direct-to-LDS load writes 1 KiB per wave instruction, contiguous, so rows
 // are not padded: 16-byte chunks are XOR-swizzled within each row instead,
 // which keeps the K operand reads (16 rows, one chunk each) and the
