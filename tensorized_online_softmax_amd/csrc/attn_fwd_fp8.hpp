@@ -429,9 +429,12 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_fp8(FwdArgs a) {
 
   // ---- epilogue of an item: O / l (l: the sum of hi + lo, so the 2^8
   // cancels), lse = lse_scale * ref + ln(l_exact / 2^8).  finish() puts this
-  // wave's O rows in its staging area (chunk c of row r at c xor (r mod 16));
-  // flush() stores them as whole rows after the next item's prologue wait.
+  // wave's O rows in its staging area (the 16-bit kernel's layout: chunk c of
+  // row r at c xor ((r / rows per 256 bytes) mod chunks per row), 8-byte halves
+  // swapped when r / 16 is odd); flush() stores them as whole rows after the
+  // next item's prologue wait.
   constexpr int OCPR = ORB / 16;               // 16-byte chunks per O row
+  constexpr int ORPB = 256 / ORB;              // O rows per 256 bytes (1 or 2)
   char* const stg = smem + 2 * kRing * BLK + w * SB;
   __bf16* o_rows = nullptr;
   float* lse_rows = nullptr;
@@ -450,7 +453,7 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_fp8(FwdArgs a) {
         bf16x4 ov;
 #pragma unroll
         for (int u = 0; u < 4; ++u) ov[u] = (__bf16)(oacc[mt][4 * g + u] * inv);
-        *(bf16x4*)(stg + sr * ORB + 16 * ((4 * mt + g) ^ (sr % OCPR)) + 8 * hf) = ov;
+        *(bf16x4*)(stg + sr * ORB + 16 * ((4 * mt + g) ^ ((sr / ORPB) % OCPR)) + 8 * (hf ^ ((sr >> 4) & 1))) = ov;
       }
     const int wq0 = q0 + 32 * w;
     o_rows = (__bf16*)a.o + head + (size_t)wq0 * D;
@@ -467,7 +470,8 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_fp8(FwdArgs a) {
 #pragma unroll
     for (int k = 0; k < 32 / RPI; ++k) {
       const int r = k * RPI + L / OCPR, cc = L % OCPR;
-      const u32x4 v = *(const u32x4*)(stg + r * ORB + 16 * (cc ^ (r % OCPR)));
+      u32x4 v = *(const u32x4*)(stg + r * ORB + 16 * (cc ^ ((r / ORPB) % OCPR)));
+      if ((r >> 4) & 1) v = __builtin_shufflevector(v, v, 2, 3, 0, 1);
       if (r < o_nrows) *(u32x4*)(o_rows + (size_t)r * D + 8 * cc) = v;
     }
     if (lse_rows != nullptr && hf == 0 && ln < o_nrows) lse_rows[ln] = lse_out;

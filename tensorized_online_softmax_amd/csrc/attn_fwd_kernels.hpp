@@ -732,10 +732,13 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_h16(FwdArgs a) {
 
   // ---- epilogue of an item: l, O / l, lse (reading R-7: lse = scale*ref + ln l).
   // finish() computes them and puts this wave's O rows (32 x D) in its LDS
-  // staging area, row r's 16-byte chunk c at position c xor (r mod CPR);
-  // flush() stores them, whole rows per instruction, after the next item's
-  // prologue wait, so that the stores do not hold up that wait.
+  // staging area: with q = r / RPB (RPB rows per 256 bytes), row r's 16-byte
+  // chunk c sits at position c xor (q mod CPR), its two 8-byte halves swapped
+  // when r / 16 is odd, so that the 32 lanes of each 8-byte write pass cover
+  // all 64 banks.  flush() stores them, whole rows per instruction, after the
+  // next item's prologue wait, so that the stores do not hold up that wait.
   constexpr int CPR = RB / 16;                  // 16-byte chunks per row
+  constexpr int RPB = 256 / RB;                 // rows per 256 bytes (1 or 2)
   char* const stg = w < 4 ? smem + 2 * BLK + w * SB : smem + 2 * kRing * BLK + (w - 4) * SB;
   E* o_rows = nullptr;      // the finished item's first row of this wave (uniform)
   float* lse_rows = nullptr;
@@ -764,7 +767,7 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_h16(FwdArgs a) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) ov[u] = (E)(oacc[mt][4 * g + u] * inv);
         if (!direct)
-          *(ev4*)(stg + sr * RB + 16 * ((4 * mt + g) ^ (sr % CPR)) + 8 * hf) = ov;
+          *(ev4*)(stg + sr * RB + 16 * ((4 * mt + g) ^ ((sr / RPB) % CPR)) + 8 * (hf ^ ((sr >> 4) & 1))) = ov;
         else if (qvalid)
           *(ev4*)((E*)a.o + head + (size_t)qrow * D + 32 * mt + 8 * g + 4 * hf) = ov;
       }
@@ -783,7 +786,8 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_h16(FwdArgs a) {
 #pragma unroll
     for (int k = 0; k < 32 / RPI; ++k) {
       const int r = k * RPI + L / CPR, cc = L % CPR;
-      const ev8 v = *(const ev8*)(stg + r * RB + 16 * (cc ^ (r % CPR)));
+      ev8 v = *(const ev8*)(stg + r * RB + 16 * (cc ^ ((r / RPB) % CPR)));
+      if ((r >> 4) & 1) v = __builtin_shufflevector(v, v, 4, 5, 6, 7, 0, 1, 2, 3);
       if (r < o_nrows && !(X == 64 && w == 7 && r == 31)) *(ev8*)(o_rows + (size_t)r * D + 8 * cc) = v;
     }
     if (lse_rows != nullptr && hf == 0 && ln < o_nrows) lse_rows[ln] = lse_out;
