@@ -369,6 +369,9 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_fp8(FwdArgs a) {
     step_loads(j, XING);
     float alpha = 1.0f, nb = 0.0f;
     pe[0] = pe[1] = 0.0f;
+    // phase A at raised wave priority, phase B at the default (as in the
+    // 16-bit kernel: of the two waves of a SIMD, the one behind issues first)
+    __builtin_amdgcn_s_setprio(1);
     // phase A: QK g = 2 kk + t, operands read one instruction ahead
     i32x8 kop = kread(kslot, 0, 0);
 #pragma unroll
@@ -391,6 +394,7 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_fp8(FwdArgs a) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    __builtin_amdgcn_s_setprio(0);
     // phase B: per M tile one V operand for the hi and the lo product
     i32x8 vop = vread(vslot, 0), vop_hold = {};
 #pragma unroll

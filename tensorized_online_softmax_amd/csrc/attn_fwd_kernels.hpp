@@ -695,6 +695,10 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_h16(FwdArgs a) {
     for (int g = 0; g < LA; ++g) kop[g] = kread(kt, g);
     float alpha = 1.0f, nb = 0.0f;
     sums_reset();
+    // Phase A runs at raised wave priority and phase B at the default: when
+    // the two waves of a SIMD are in different phases, the one still in phase
+    // A (behind) is issued first, which keeps the pair in step.
+    __builtin_amdgcn_s_setprio(1);
     // phase A: units 0..EA-1 in the chunks after the chain
 #pragma unroll
     for (int g = 0; g < NQK; ++g) {
@@ -708,6 +712,7 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_h16(FwdArgs a) {
         if (MAXC + k * (NQK - MAXC) / EA == g) exp_unit(k, c0, c1, P[cur], nb);
       __builtin_amdgcn_sched_barrier(0);
     }
+    __builtin_amdgcn_s_setprio(0);
     // phase B: units EA..15 spread over the chunks
 #pragma unroll
     for (int i = 0; i < NPV; ++i) {
