@@ -27,7 +27,11 @@ CXXFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
 # instruction it otherwise puts in front of every maximum and fuse the
 # cross-lane maxima with their DPP moves.  The argument checks in tos_api.hip
 # test for NaN and keep the default.
-KERNEL_FLAGS = ["-fno-honor-nans"]
+#
+# -fno-signed-zeros: the kernels never depend on the sign of a zero (O, l and
+# lse are the same for -0 and +0), which lets the first addition into a zeroed
+# sum fold away.
+KERNEL_FLAGS = ["-fno-honor-nans", "-fno-signed-zeros"]
 
 
 def _compile(src, verbose):

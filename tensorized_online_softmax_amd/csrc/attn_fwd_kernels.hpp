@@ -498,15 +498,17 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_h16(FwdArgs a) {
   auto max_part = [&](int q, const f32x16& s0, const f32x16& s1) {
     const f32x16& sv = (q / 2) ? s1 : s0;
     const int r0 = 8 * (q % 2);
+    // one v_max3 per two logits (the compiler would build a tree of v_max
+    // and v_max3 instead: 5 instructions per 8 logits rather than 4)
     float m = fmax_raw(sv[r0], sv[r0 + 1]);
 #pragma unroll
-    for (int r = r0 + 2; r < r0 + 8; r += 2) m = fmax_raw(m, fmax_raw(sv[r], sv[r + 1]));
+    for (int r = r0 + 2; r < r0 + 8; r += 2) m = fmax3_raw(m, sv[r], sv[r + 1]);
     bm4[q] = m;
   };
   // steps 2-3: running row maxima and the lane-pair combine; rows past N stay
   // out of the tile maximum
   auto max_combine = [&]() {
-    float bm = fmax_raw(fmax_raw(bm4[0], bm4[1]), fmax_raw(bm4[2], bm4[3]));
+    float bm = fmax_raw(fmax3_raw(bm4[0], bm4[1], bm4[2]), bm4[3]);
     bm = qvalid ? bm : -__builtin_inff();
     row_max_update(st, bm);
   };
@@ -561,13 +563,25 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_h16(FwdArgs a) {
   // sum of the rounded P~ that the product consumes normalises O, so O / l
   // stays a weighted average of V rows (16-bit rounding of P~ then cancels to
   // first order instead of adding to the error of O).
+  // A unit runs in three stages, so that a steady step can issue them in
+  // different chunks and keep each stage's inputs ready when it issues:
+  // (1) the FMA Z = c*S - c*ref, (2) exp2, (3) both sums and the packing.
   float pe[2], ps[2];
+  float uz[16][2], up[16][2];   // per unit: Z, then P~ (registers, unrolled)
   auto sums_reset = [&]() { pe[0] = pe[1] = ps[0] = ps[1] = 0.0f; };
-  auto exp_unit = [&](int k, const f32x16& s0, const f32x16& s1, ev8* pk, float nb) {
+  auto unit_fma = [&](int k, const f32x16& s0, const f32x16& s1, float nb) {
     const int t = k / 8, r = 2 * (k % 8);
     const f32x16& sv = t ? s1 : s0;
-    const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r], c, nb));
-    const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r + 1], c, nb));
+    uz[k][0] = __builtin_fmaf(sv[r], c, nb);
+    uz[k][1] = __builtin_fmaf(sv[r + 1], c, nb);
+  };
+  auto unit_exp = [&](int k) {
+    up[k][0] = __builtin_amdgcn_exp2f(uz[k][0]);
+    up[k][1] = __builtin_amdgcn_exp2f(uz[k][1]);
+  };
+  auto unit_sum_pack = [&](int k, ev8* pk) {
+    const int t = k / 8, r = 2 * (k % 8);
+    const float p0 = up[k][0], p1 = up[k][1];
     pe[t] += p0;
     pe[t] += p1;
     ev2 w;
@@ -576,6 +590,11 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_h16(FwdArgs a) {
     pk[2 * t + r / 8][r % 8] = w[0];
     pk[2 * t + r / 8][r % 8 + 1] = w[1];
     if constexpr (!ROWSUM_MFMA) ps[t] = Elem16<E>::dot2(w, ones2, ps[t]);
+  };
+  auto exp_unit = [&](int k, const f32x16& s0, const f32x16& s1, ev8* pk, float nb) {
+    unit_fma(k, s0, s1, nb);
+    unit_exp(k);
+    unit_sum_pack(k, pk);
   };
   // the block's sums into the running ones (which absorb alpha here; O and the
   // MFMA row sum get alpha at the end of the step)
@@ -661,12 +680,30 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_h16(FwdArgs a) {
   //                                     dependency chain left to wait on)
   // The chain (d=128: parts 0-1 | 2-3 | combine | tile max | advance; d=64:
   // parts 0-3 | combine, tile max | advance) takes the first chunks of A;
-  // units are spread evenly over the chunks after it and over B.  Operand
+  // units are spread evenly over the chunks after it and over B.  At d=128 a
+  // unit's three stages go to chunks c, c+2 and c+4 of the step (clamped to
+  // its last chunk), so that no stage waits for the one before it.  Operand
   // reads run LA instructions ahead; S and P~ alternate between the two
   // register sets.
   constexpr int MAXC = NQK >= 16 ? 5 : 3;      // phase-A chunks of the maximum chain
   constexpr int EA = NQK >= 16 ? 6 : 3;        // exponential units in phase A
   constexpr int LA = 3;                        // operand read lookahead
+  constexpr int SKEW = NQK >= 16 ? 2 : 0;      // chunks between a unit's stages
+  constexpr int LASTC = NQK + NPV - 1;         // last chunk of a step
+  // chunk of unit k's first stage
+  auto unit_chunk = [&](int k) -> int {
+    return k < EA ? MAXC + k * (NQK - MAXC) / EA : NQK + (k - EA) * NPV / (16 - EA);
+  };
+  // the unit stages that fall in chunk g (in stage order for each unit)
+  auto unit_stages = [&](int g, const f32x16& c0, const f32x16& c1, ev8* pk, float nb) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int uc = unit_chunk(k);
+      if (uc == g) unit_fma(k, c0, c1, nb);
+      if (min(uc + SKEW, LASTC) == g) unit_exp(k);
+      if (min(uc + 2 * SKEW, LASTC) == g) unit_sum_pack(k, pk);
+    }
+  };
   auto max_chunk = [&](int i, f32x16& c0, f32x16& c1, float& alpha, float& nb) {
     if constexpr (NQK >= 16) {
       if (i == 0) { max_part(0, c0, c1); max_part(1, c0, c1); }
@@ -699,7 +736,7 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_h16(FwdArgs a) {
     // the two waves of a SIMD are in different phases, the one still in phase
     // A (behind) is issued first, which keeps the pair in step.
     __builtin_amdgcn_s_setprio(1);
-    // phase A: units 0..EA-1 in the chunks after the chain
+    // phase A: units 0..EA-1 start in the chunks after the chain
 #pragma unroll
     for (int g = 0; g < NQK; ++g) {
       const ev8 av = kop[g % LA];
@@ -707,21 +744,17 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_h16(FwdArgs a) {
       else vop[(g + LA - NQK) % LA] = vread(vt, g + LA - NQK);
       qk_mfma(g, av, n0, n1);
       max_chunk(g, c0, c1, alpha, nb);
-#pragma unroll
-      for (int k = 0; k < EA; ++k)
-        if (MAXC + k * (NQK - MAXC) / EA == g) exp_unit(k, c0, c1, P[cur], nb);
+      unit_stages(g, c0, c1, P[cur], nb);
       __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_s_setprio(0);
-    // phase B: units EA..15 spread over the chunks
+    // phase B: units EA..15 start spread over the chunks
 #pragma unroll
     for (int i = 0; i < NPV; ++i) {
       const ev8 av = vop[i % LA];
       if (i + LA < NPV) vop[i % LA] = vread(vt, i + LA);
       pv_mfma(i, av, P[nxt]);
-#pragma unroll
-      for (int k = EA; k < 16; ++k)
-        if ((k - EA) * NPV / (16 - EA) == i) exp_unit(k, c0, c1, P[cur], nb);
+      unit_stages(NQK + i, c0, c1, P[cur], nb);
       __builtin_amdgcn_sched_barrier(0);
     }
     sums_commit(alpha);

@@ -19,6 +19,16 @@ namespace tos {
 
 __device__ __forceinline__ float fmax_raw(float a, float b) { return __builtin_fmaxf(a, b); }
 __device__ __forceinline__ float fmin_raw(float a, float b) { return __builtin_fminf(a, b); }
+// max(a, b, c) as one v_max3_f32 (finite inputs)
+__device__ __forceinline__ float fmax3_raw(float a, float b, float c) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  float m;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(m) : "v"(a), "v"(b), "v"(c));
+  return m;
+#else
+  return __builtin_fmaxf(__builtin_fmaxf(a, b), c);
+#endif
+}
 
 // value of the other lane of the pair (L, L xor 32), combined with op
 template <typename Op>
