@@ -273,12 +273,12 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_fp8(FwdArgs a) {
     const int r0 = 8 * (q % 2);
     float m = fmax_raw(sv[r0], sv[r0 + 1]);
 #pragma unroll
-    for (int r = r0 + 2; r < r0 + 8; r += 2) m = fmax_raw(m, fmax_raw(sv[r], sv[r + 1]));
+    for (int r = r0 + 2; r < r0 + 8; r += 2) m = fmax3_raw(m, sv[r], sv[r + 1]);
     m4[q] = m;
   };
   float ref_new = 0.0f;
   auto max_combine = [&]() {
-    float bm = fmax_raw(fmax_raw(m4[0], m4[1]), fmax_raw(m4[2], m4[3]));
+    float bm = fmax_raw(fmax3_raw(m4[0], m4[1], m4[2]), m4[3]);
     bm = qvalid ? bm : -__builtin_inff();
     row_max_update(st, bm);
   };
@@ -291,16 +291,26 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_fp8(FwdArgs a) {
   // steps 4-7 for registers r..r+3 of tile u (unit k: u = k / 4, r = 4 (k % 4)):
   // 2^8 P~ = exp2(c*S - c*ref + 8) as hi + lo e4m3 terms (operand dword 4u + r/4),
   // and the unrounded row sum
+  // (in three stages, as in the 16-bit kernel, so that a steady step can put
+  // them in different chunks: the FMAs, the exponentials, then the sum and
+  // the hi / lo packing)
   float pe[2];
-  auto exp_unit = [&](int k, const f32x16& s0, const f32x16& s1, i32x8& pk, i32x8& pl, float nb) {
+  float fz[8][4], fp[8][4];   // per unit: Z, then 2^8 P~ (registers, unrolled)
+  auto unit_fma = [&](int k, const f32x16& s0, const f32x16& s1, float nb) {
     const int u = k / 4, r = 4 * (k % 4);
     const f32x16& sv = u ? s1 : s0;
-    float p[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r + e], c, nb));
-      pe[u] += p[e];
-    }
+    for (int e = 0; e < 4; ++e) fz[k][e] = __builtin_fmaf(sv[r + e], c, nb);
+  };
+  auto unit_exp = [&](int k) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) fp[k][e] = __builtin_amdgcn_exp2f(fz[k][e]);
+  };
+  auto unit_sum_pack = [&](int k, i32x8& pk, i32x8& pl) {
+    const int u = k / 4, r = 4 * (k % 4);
+    const float* p = fp[k];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pe[u] += p[e];
     int wd = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
     wd = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], wd, true);
     pk[4 * u + r / 4] = wd;
@@ -309,6 +319,11 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_fp8(FwdArgs a) {
     int wl = __builtin_amdgcn_cvt_pk_fp8_f32(p[0] - h01[0], p[1] - h01[1], 0, false);
     wl = __builtin_amdgcn_cvt_pk_fp8_f32(p[2] - h23[0], p[3] - h23[1], wl, true);
     pl[4 * u + r / 4] = wl;
+  };
+  auto exp_unit = [&](int k, const f32x16& s0, const f32x16& s1, i32x8& pk, i32x8& pl, float nb) {
+    unit_fma(k, s0, s1, nb);
+    unit_exp(k);
+    unit_sum_pack(k, pk, pl);
   };
   auto rescale = [&](float alpha) {
     if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
@@ -412,10 +427,15 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_fp8(FwdArgs a) {
       } else {
         lacc = mfma_f8(ones, i == 2 * NMT ? PH[nxt] : PL[nxt], lacc);
       }
-      // the 8 exponential units: one per chunk at d = 128, spread over the
-      // 6 chunks at d = 64
+      // the 8 exponential units: one per chunk at d = 128 (unit i's three
+      // stages in chunks i, i+1 and i+2), spread over the 6 chunks at d = 64
       if constexpr (D == 128) {
-        if (i < 8) exp_unit(i, c0, c1, PH[cur], PL[cur], nb);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          if (k == i) unit_fma(k, c0, c1, nb);
+          if (k + 1 == i) unit_exp(k);
+          if (k + 2 == i) unit_sum_pack(k, PH[cur], PL[cur]);
+        }
       } else {
 #pragma unroll
         for (int k = 0; k < 8; ++k)
