@@ -1,9 +1,11 @@
-// attn_fwd_kernels.hpp -- fused attention forward kernels for gfx950 (MI355X).
+// attn_fwd_kernels.hpp -- fused attention forward kernels for gfx950 (MI355X):
+// attn_fwd_h16 (bf16 and fp16 inputs: persistent 8-wave workgroups of 256
+// query rows, 64-key blocks in LDS rings; described at its definition) and
+// attn_fwd_f32 (fp32 inputs: 4-wave workgroups of 128 query rows, one 64-key
+// block at a time in LDS).  attn_fwd_fp8.hpp holds the fp8 kernel.
 //
-// One workgroup = 4 waves = 128 query rows of one (batch, head); each wave owns
-// 32 query rows.  Keys stream through LDS in blocks of 64 (double-buffered: the
-// global loads of block j+1 are in flight while block j is computed).  Per key
-// block each wave runs the fused-attention iteration of FlashAttention-T
+// In both, each wave owns 32 query rows, and per key block each wave runs the
+// fused-attention iteration of FlashAttention-T
 // (section A3, Fig 2(a)) with the tensorized online softmax (section A2,
 // Algorithm 1):
 //   S^T = K_j Q^T                          (MFMA; Q held in registers)
