@@ -189,19 +189,27 @@ def grid_sweep(dtypes, steps, warmup):
 
 
 # The ablation's knob settings, after FlashAttention-T's evaluation (section
-# A4, Fig 9 and Fig 10: FA2, FA2 + Max16, AllTensor, FA-T): name, X, row-sum
-# split, schedule.  The pages' AllTensor puts scaling and FMA on the tensor
-# unit; gfx950 has no TF32 matrix instruction, and the setting here scales O
-# with fp32 products (the FMA before exp2 stays a vector instruction).
+# A4, Fig 9 and Fig 10: FA2, FA2 + Max16, AllTensor, FA-T) and its
+# tensor-vector split (section A2, Fig 6): name, X, softmax split, schedule,
+# matrix-unit share.  The pages' AllTensor puts scaling, FMA and the row sum on
+# the tensor unit; gfx950 has no TF32 matrix instruction, so here the scaling
+# and the FMA are fp32 products.
 ABLATION = [
-    ("per_row_sequential", 1, "valu", "sequential"),     # FA2 analog
-    ("per_row_cosched", 1, "valu", "cosched"),
-    ("tile16_cosched", 16, "valu", "cosched"),           # Max16 analog
-    ("tile32_sequential", 32, "valu", "sequential"),
-    ("tile32_cosched", 32, "valu", "cosched"),           # FA-T analog (the default)
-    ("tile64_cosched", 64, "valu", "cosched"),           # tiles of two waves
-    ("tile32_rowsum_mfma", 32, "rowsum_mfma", "cosched"),
-    ("tile32_scale_mfma", 32, "scale_mfma", "cosched"),  # O rescale on the matrix unit
+    ("per_row_sequential", 1, "valu", "sequential", None),     # FA2 analog
+    ("per_row_cosched", 1, "valu", "cosched", None),
+    ("tile16_cosched", 16, "valu", "cosched", None),           # Max16 analog
+    ("tile32_sequential", 32, "valu", "sequential", None),
+    ("tile32_cosched", 32, "valu", "cosched", None),           # FA-T analog (the default)
+    ("tile64_cosched", 64, "valu", "cosched", None),           # tiles of two waves
+    ("tile32_rowsum_mfma", 32, "rowsum_mfma", "cosched", None),
+    ("tile32_rowsum_1_4", 32, "rowsum_mfma", "cosched", (1, 4)),
+    ("tile32_rowsum_1_2", 32, "rowsum_mfma", "cosched", (1, 2)),
+    ("tile32_rowsum_3_4", 32, "rowsum_mfma", "cosched", (3, 4)),
+    ("tile32_scale_mfma", 32, "scale_mfma", "cosched", None),  # O rescale on the matrix unit
+    ("tile32_hsplit_1_4", 32, "hsplit", "cosched", (1, 4)),
+    ("tile32_hsplit_1_2", 32, "hsplit", "cosched", (1, 2)),
+    ("tile32_vsplit_1_2", 32, "vsplit", "cosched", (1, 2)),
+    ("tile32_all_mfma", 32, "all_mfma", "cosched", None),      # AllTensor analog
 ]
 
 
@@ -228,10 +236,11 @@ def ablation(workload, steps, warmup, reps=3):
     warm = max(2, min(warmup, 5))
     times = [[] for _ in ABLATION]
     for _ in range(reps):
-        for si, (name, x, split, sched) in enumerate(ABLATION):
+        for si, (name, x, split, sched, share) in enumerate(ABLATION):
             def f():
                 binding.attn_fwd(q, k, v, causal=w.causal, scale=w.scale, dtype=w.dtype,
-                                 x_tile=x, split=split, schedule=sched, out=o, lse=lse)
+                                 x_tile=x, split=split, schedule=sched, share=share,
+                                 out=o, lse=lse)
             for _ in range(warm):
                 f()
             ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -243,9 +252,10 @@ def ablation(workload, steps, warmup, reps=3):
             torch.cuda.synchronize()
             times[si] += [a.elapsed_time(b) / 1e3 for a, b in ev]
     med = [sorted(t)[len(t) // 2] for t in times]
-    for (name, x, split, sched), m, t in zip(ABLATION, med, times):
+    for (name, x, split, sched, share), m, t in zip(ABLATION, med, times):
         tf = w.flops() / m / 1e12
         print(json.dumps({"workload": w.name, "setting": name, "x_tile": x, "softmax_split": split,
+                          "share": f"{share[0]}/{share[1]}" if share else None,
                           "schedule": sched, "launches": len(t), "median_us": round(m * 1e6, 2),
                           "tflops": round(tf, 1), "frac": round(tf / PEAK_TFLOPS[w.dtype], 4),
                           "speedup_over_first": round(med[0] / m, 4)}), flush=True)
@@ -257,7 +267,10 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="causal_bf16")
-    ap.add_argument("--split", default="valu", choices=["valu", "rowsum_mfma", "scale_mfma"])
+    ap.add_argument("--split", default="valu",
+                    choices=["valu", "rowsum_mfma", "scale_mfma", "hsplit", "vsplit", "all_mfma"])
+    ap.add_argument("--share", default=None, metavar="NUM/DEN",
+                    help="the matrix unit's share of the --split value (e.g. 1/2)")
     ap.add_argument("--schedule", default="cosched", choices=["cosched", "sequential"],
                     help="sequential: the no-co-scheduling ablation (16-bit inputs)")
     ap.add_argument("--ablation", action="store_true",
@@ -311,10 +324,12 @@ def main():
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
     descale = inp["descale"] if w.dtype == "fp8" else None
 
+    share = tuple(int(x) for x in args.share.split("/")) if args.share else None
+
     def step():
         binding.attn_fwd(q, k, v, causal=w.causal, scale=w.scale, dtype=w.dtype,
                          x_tile=x_tile, split=args.split, fallback=fallback,
-                         descale=descale, out=o, lse=lse, schedule=args.schedule)
+                         descale=descale, out=o, lse=lse, schedule=args.schedule, share=share)
 
     for _ in range(args.warmup):
         step()

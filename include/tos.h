@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define TOS_VERSION 1
+#define TOS_VERSION 2
 
 typedef enum {
     TOS_OK = 0,
@@ -62,22 +62,47 @@ typedef enum {
                           bf16, with the fp16 matrix instructions)                */
 } tos_dtype;
 
-/* How the softmax row sum l is computed (FlashAttention-T section A2,
- * "row-sum reduction", Fig 5(b)). */
+/* Where the element-wise softmax steps run: the vector unit or the matrix unit
+ * (FlashAttention-T section A2: repurposed matrix instructions for the row sum,
+ * Fig 5(b), and for scaling / fused multiply-add, Fig 5(a); the tensor-vector
+ * split of Fig 6).  The matrix-unit forms are fp32 products for the scaling and
+ * the FMA (gfx950 has no TF32 matrix instruction; bf16 products would round O
+ * or Z past the tolerance) and 16-bit products against an all-ones operand for
+ * the row sum.  split_num / split_den in tos_fwd_opts give the matrix unit's
+ * share where a value takes one.  bf16 and f16 only; values other than
+ * TOS_SPLIT_VALU and TOS_SPLIT_ROWSUM_MFMA need X = 32, no fallback and the
+ * co-scheduled schedule (else TOS_ERR_UNSUPPORTED). */
 typedef enum {
-    TOS_SPLIT_VALU = 0,         /* vector-unit dot products of the packed P~ pairs
-                                   with (1, 1)                                      */
-    TOS_SPLIT_ROWSUM_MFMA = 1,  /* matrix-unit contraction of the packed P~ against a
-                                   constant all-ones operand (bf16, f16; not fp32)  */
-    TOS_SPLIT_SCALE_MFMA = 2    /* VALU row sum, and the O rescale by the tile's
-                                   factor on the matrix unit (section A2, Fig 5(a):
-                                   fp32 products against alpha I).  An A/B variant:
-                                   bf16/f16, X = 32, fallback off, co-scheduled
-                                   only (else TOS_ERR_UNSUPPORTED)                  */
+    TOS_SPLIT_VALU = 0,         /* everything on the vector unit (the row sum as
+                                   dot products of packed P~ pairs with (1, 1))    */
+    TOS_SPLIT_ROWSUM_MFMA = 1,  /* the row sum on the matrix unit: ones x P~^T.
+                                   With split_den > 0, only a share of each key
+                                   block's four 16-key steps (num/den, a multiple
+                                   of 1/4; < 1 needs X = 32 and no fallback), the
+                                   rest on the vector unit                         */
+    TOS_SPLIT_SCALE_MFMA = 2,   /* the O rescale by the tile's factor alpha on the
+                                   matrix unit (products against alpha I)          */
+    TOS_SPLIT_HSPLIT = 3,       /* horizontal split (Fig 6(a)): in every 32x32 tile
+                                   of S and of O, the register slices below the
+                                   share num/den (1/4, 1/2 or 3/4) run
+                                   Z = c*S - c*m^ and the O rescale on the matrix
+                                   unit, the rest on the vector unit; the same
+                                   share of the row-sum steps on the matrix unit  */
+    TOS_SPLIT_VSPLIT = 4,       /* vertical split (Fig 6(b)) with share 1/2: the
+                                   first of a block's two S tiles and the first
+                                   half of O's tiles on the matrix unit, and half
+                                   the row-sum steps                               */
+    TOS_SPLIT_ALL_MFMA = 5      /* every step that has a matrix form on the matrix
+                                   unit: Z (the offset -c*m^ carried into the
+                                   accumulator by one more product), the O rescale
+                                   and the row sum (the pages' AllTensor variant)  */
 } tos_softmax_split;
 /* Either way l sums the rounded P~ that the P~V product consumes, and a separate
- * unrounded fp32 sum gives lse.  TOS_FP8_E4M3 has no vector form for e4m3
- * pairs: its rounded sum is always the matrix-unit one, whatever the option. */
+ * unrounded fp32 sum gives lse.  Z and the O rescale take their matrix form in
+ * the steady steps of the pipeline; a wave's first and last key blocks (where
+ * logits may be masked) keep the vector form.  TOS_FP8_E4M3 has no vector form
+ * for e4m3 pairs: its rounded sum is always the matrix-unit one, and it accepts
+ * only TOS_SPLIT_VALU and TOS_SPLIT_ROWSUM_MFMA (both meaning that). */
 
 /* Instruction schedule of the 16-bit kernels (an ablation of FlashAttention-T
  * section A2, "tensor-vector parallelism", Fig 7, and of its evaluation, Fig 9
@@ -114,8 +139,10 @@ typedef struct {
                               TOS_ERR_UNSUPPORTED                                  */
     int softmax_split;     /* a tos_softmax_split value                             */
     int fallback;          /* a tos_fallback value                                  */
-    float fallback_tau;    /* AUTO threshold in log2 units; 0 = default (100 for
-                              f32/bf16 P~, 24 for f16 P~, 12 for e4m3 P~)           */
+    float fallback_tau;    /* AUTO threshold in log2 units, at most 126; 0 =
+                              default (100 for f32/bf16 P~, 24 for f16 P~, 12 for
+                              e4m3 P~).  The switch rescales by up to 2^tau, which
+                              must stay finite in fp32                             */
     float q_descale;       /* fp8 only: real value = descale * stored code; > 0    */
     float k_descale;
     float v_descale;
@@ -123,6 +150,8 @@ typedef struct {
                               X-row tile that ran with per-row maxima (AUTO switch
                               or FORCE).  The caller zeroes it.                    */
     int schedule;          /* a tos_schedule value                                  */
+    int split_num;         /* the matrix unit's share split_num / split_den of the */
+    int split_den;         /* softmax_split value (0 / 0: the value's default)     */
 } tos_fwd_opts;
 
 /*

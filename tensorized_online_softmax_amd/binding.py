@@ -13,7 +13,8 @@ LIB_PATH = os.path.join(_PKG, "libtos.so")
 
 TOS_OK, TOS_ERR_INVALID_ARG, TOS_ERR_UNSUPPORTED, TOS_ERR_HIP = 0, 1, 2, 3
 TOS_F32, TOS_BF16, TOS_FP8_E4M3, TOS_F16 = 0, 1, 2, 3
-TOS_SPLIT_VALU, TOS_SPLIT_ROWSUM_MFMA, TOS_SPLIT_SCALE_MFMA = 0, 1, 2
+(TOS_SPLIT_VALU, TOS_SPLIT_ROWSUM_MFMA, TOS_SPLIT_SCALE_MFMA, TOS_SPLIT_HSPLIT, TOS_SPLIT_VSPLIT,
+ TOS_SPLIT_ALL_MFMA) = range(6)
 TOS_FALLBACK_OFF, TOS_FALLBACK_AUTO, TOS_FALLBACK_FORCE = 0, 1, 2
 TOS_SCHEDULE_COSCHED, TOS_SCHEDULE_SEQUENTIAL = 0, 1
 
@@ -26,7 +27,8 @@ class tos_fwd_opts(ctypes.Structure):
                 ("softmax_split", ctypes.c_int), ("fallback", ctypes.c_int),
                 ("fallback_tau", ctypes.c_float), ("q_descale", ctypes.c_float),
                 ("k_descale", ctypes.c_float), ("v_descale", ctypes.c_float),
-                ("fallback_tiles", ctypes.c_void_p), ("schedule", ctypes.c_int)]
+                ("fallback_tiles", ctypes.c_void_p), ("schedule", ctypes.c_int),
+                ("split_num", ctypes.c_int), ("split_den", ctypes.c_int)]
 
 
 class TosError(RuntimeError):
@@ -112,14 +114,19 @@ def tos_version():
 
 _DTYPE_CODES = {"f32": TOS_F32, "bf16": TOS_BF16, "fp8": TOS_FP8_E4M3, "f16": TOS_F16}
 _SPLITS = {"valu": TOS_SPLIT_VALU, "rowsum_mfma": TOS_SPLIT_ROWSUM_MFMA,
-           "scale_mfma": TOS_SPLIT_SCALE_MFMA}
+           "scale_mfma": TOS_SPLIT_SCALE_MFMA, "hsplit": TOS_SPLIT_HSPLIT,
+           "vsplit": TOS_SPLIT_VSPLIT, "all_mfma": TOS_SPLIT_ALL_MFMA}
 _FALLBACKS = {"off": TOS_FALLBACK_OFF, "auto": TOS_FALLBACK_AUTO, "force": TOS_FALLBACK_FORCE}
 _SCHEDULES = {"cosched": TOS_SCHEDULE_COSCHED, "sequential": TOS_SCHEDULE_SEQUENTIAL}
 
 
 def make_opts(x_tile=32, split="valu", fallback="off", tau=0.0, descale=None,
-              fallback_tiles=None, schedule="cosched"):
+              fallback_tiles=None, schedule="cosched", share=None):
+    """Options for tos_attn_fwd.  split names a tos_softmax_split value;
+    share = (num, den) is the matrix unit's share of it (None: the default)."""
     op = tos_fwd_opts_default()
+    if share is not None:
+        op.split_num, op.split_den = int(share[0]), int(share[1])
     op.x_tile = int(x_tile)
     op.softmax_split = _SPLITS[split]
     op.fallback = _FALLBACKS[fallback]
@@ -131,9 +138,77 @@ def make_opts(x_tile=32, split="valu", fallback="off", tau=0.0, descale=None,
     return op
 
 
+def _torch_dtypes():
+    import torch
+    return {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16,
+            "fp8": torch.float8_e4m3fn}
+
+
+def out_dtype(dtype):
+    """torch dtype of O for an input dtype name (fp8 inputs give bf16 O)."""
+    import torch
+    return {"f32": torch.float32, "f16": torch.float16}.get(dtype, torch.bfloat16)
+
+
+def check_tensors(q, k, v, dtype=None, out=None, lse=None, fallback_tiles=None):
+    """Checks what the C ABI cannot see from raw pointers, before any launch:
+    q, k, v are contiguous [B, H, N, d] tensors of the named dtype on one CUDA
+    device; out (if given) is a contiguous [B, H, N, d] tensor of O's dtype there;
+    lse (if given) a contiguous float32 [B, H, N] tensor there; fallback_tiles
+    (if given) an int32 tensor of at least one element there.  Raises
+    ValueError on any mismatch; returns (B, H, N, d, dtype name)."""
+    tdt = _torch_dtypes()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not hasattr(t, "dim") or t.dim() != 4:
+            raise ValueError(f"{name} must be a 4-D tensor [B, H, N, d]")
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError(f"q, k, v shapes differ: {tuple(q.shape)}, {tuple(k.shape)}, "
+                         f"{tuple(v.shape)}")
+    if dtype is None:
+        inv = {t: n for n, t in tdt.items()}
+        if q.dtype not in inv:
+            raise ValueError(f"unsupported input dtype {q.dtype}")
+        dtype = inv[q.dtype]
+    if dtype not in tdt:
+        raise ValueError(f"unknown dtype name {dtype!r}")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != tdt[dtype]:
+            raise ValueError(f"{name} is {t.dtype}, dtype {dtype!r} needs {tdt[dtype]}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous (got strides {t.stride()})")
+    B, H, N, d = (int(x) for x in q.shape)
+    if out is not None:
+        if tuple(out.shape) != (B, H, N, d) or out.dtype != out_dtype(dtype):
+            raise ValueError(f"out must be {out_dtype(dtype)} [B, H, N, d] = {(B, H, N, d)}, "
+                             f"got {out.dtype} {tuple(out.shape)}")
+        if not out.is_contiguous():
+            raise ValueError("out must be contiguous")
+    if lse is not None:
+        import torch
+        if tuple(lse.shape) != (B, H, N) or lse.dtype != torch.float32:
+            raise ValueError(f"lse must be float32 [B, H, N] = {(B, H, N)}, "
+                             f"got {lse.dtype} {tuple(lse.shape)}")
+        if not lse.is_contiguous():
+            raise ValueError("lse must be contiguous")
+    if fallback_tiles is not None and not isinstance(fallback_tiles, int):
+        import torch
+        if fallback_tiles.dtype != torch.int32 or fallback_tiles.numel() < 1:
+            raise ValueError("fallback_tiles must be an int32 tensor of at least one element")
+    tensors = [("q", q), ("k", k), ("v", v)] + [(n, t) for n, t in (
+        ("out", out), ("lse", lse), ("fallback_tiles", fallback_tiles))
+        if t is not None and not isinstance(t, int)]
+    for name, t in tensors:
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a CUDA (HIP) tensor, got device {t.device}")
+    devs = {t.device for _, t in tensors}
+    if len(devs) != 1:
+        raise ValueError(f"every tensor must be on one device, got {sorted(map(str, devs))}")
+    return B, H, N, d, dtype
+
+
 def attn_fwd(q, k, v, causal=False, scale=None, dtype=None, x_tile=32, split="valu",
              fallback="off", tau=0.0, descale=None, with_lse=True, fallback_tiles=None,
-             out=None, lse=None, stream=None, schedule="cosched"):
+             out=None, lse=None, stream=None, schedule="cosched", share=None):
     """Allocate O (and lse) with torch and run tos_attn_fwd on the current stream.
 
     q, k, v: contiguous CUDA tensors [B, H, N, d] of float32, bfloat16, float16
@@ -141,21 +216,17 @@ def attn_fwd(q, k, v, causal=False, scale=None, dtype=None, x_tile=32, split="va
     Returns (o, lse); lse is None when with_lse is False.
     """
     import torch
-    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
-        raise ValueError("q, k, v must all be [B, H, N, d]")
-    B, H, N, d = q.shape
-    if dtype is None:
-        dtype = {torch.float32: "f32", torch.bfloat16: "bf16", torch.float16: "f16",
-                 torch.float8_e4m3fn: "fp8"}[q.dtype]
+    B, H, N, d, dtype = check_tensors(q, k, v, dtype, out, lse if with_lse else None,
+                                      fallback_tiles)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    odt = {"f32": torch.float32, "f16": torch.float16}.get(dtype, torch.bfloat16)
-    o = out if out is not None else torch.empty((B, H, N, d), dtype=odt, device=q.device)
+    o = out if out is not None else torch.empty((B, H, N, d), dtype=out_dtype(dtype),
+                                                device=q.device)
     if with_lse and lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     if not with_lse:
         lse = None
-    op = make_opts(x_tile, split, fallback, tau, descale, fallback_tiles, schedule)
+    op = make_opts(x_tile, split, fallback, tau, descale, fallback_tiles, schedule, share)
     rc = tos_attn_fwd(q, k, v, o, lse, B, H, N, d, causal, scale, _DTYPE_CODES[dtype], op,
                       stream)
     if rc != TOS_OK:

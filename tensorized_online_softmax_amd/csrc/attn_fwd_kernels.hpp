@@ -282,13 +282,49 @@ template <typename T> __device__ __forceinline__ void pin(const T& x) {
 
 template <int I> struct Int { static constexpr int value = I; };
 
+// Split plan of the element-wise softmax steps between the matrix unit and the
+// vector unit (FlashAttention-T, section A2: repurposed matrix instructions for
+// scaling / FMA (Fig 5(a)) and the row sum (Fig 5(b)); "tensor-vector split":
+// horizontal within a tile (Fig 6(a)) or vertical across a wave's tiles
+// (Fig 6(b))).  One int, fixed at compile time:
+//   bits 0-2   rs: of the 4 sixteen-key steps of a key block, those below rs
+//              take their row sum on the matrix unit (ones x P~^T)
+//   bits 3-7   z:  Z = c*S - c*ref on the matrix unit (f32 products against
+//              c*I, the offset -c*ref added by one more product): register
+//              slices s < z of both 32x32 S tiles (horizontal), or tiles t < z
+//              (vertical)
+//   bits 8-12  o:  the O rescale on the matrix unit (f32 products against
+//              alpha*I): slices s < o of every 32x32 O tile (horizontal), or
+//              tiles mt < o (vertical)
+//   bit 13     vertical
+// 0 is the all-vector plan.
+constexpr int split_plan(int rs, int z, int o, bool vertical) {
+  return rs | (z << 3) | (o << 8) | ((int)vertical << 13);
+}
+constexpr int plan_rs(int P) { return P & 7; }
+constexpr int plan_z(int P) { return (P >> 3) & 31; }
+constexpr int plan_o(int P) { return (P >> 8) & 31; }
+constexpr bool plan_vert(int P) { return (P >> 13) & 1; }
+// register slice s of S tile t / of O tile mt on the matrix unit?
+constexpr bool z_on_mfma(int P, int t, int s) { return plan_vert(P) ? t < plan_z(P) : s < plan_z(P); }
+constexpr bool o_on_mfma(int P, int mt, int s) { return plan_vert(P) ? mt < plan_o(P) : s < plan_o(P); }
+constexpr bool rs_on_mfma(int P, int step) { return step < plan_rs(P); }
+constexpr int kPlanValu = 0;
+constexpr int kPlanRowsumMfma = split_plan(4, 0, 0, false);
+constexpr int kPlanScaleMfma = split_plan(0, 0, 16, false);
+
 
 // SEQ: the sequential-schedule ablation -- every step is the generic step
 // (softmax, then QK^T, then P~V), with no interleaving inside a wave.
-// SCALE_MFMA: the O rescale on the matrix unit (an A/B variant, X = 32 only).
-template <typename E, int D, bool CAUSAL, int X, bool ROWSUM_MFMA, bool FB_AUTO, bool SEQ,
-          bool SCALE_MFMA = false>
+// PLAN: the split plan (split_plan above).  A plan that puts O rescale slices
+// on the matrix unit needs one alpha per wave (X = 32, no per-row fallback).
+template <typename E, int D, bool CAUSAL, int X, int PLAN, bool FB_AUTO, bool SEQ>
 __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_h16(FwdArgs a) {
+  constexpr int RS = plan_rs(PLAN);                   // row-sum steps on the matrix unit
+  constexpr bool ROWSUM_ANY = RS > 0, ROWSUM_ALL = RS == 4;
+  constexpr bool Z_ANY = plan_z(PLAN) > 0, O_ANY = plan_o(PLAN) > 0;
+  static_assert(!O_ANY || (X == 32 && !FB_AUTO), "matrix-unit O rescale needs one alpha per wave");
+  static_assert(plan_vert(PLAN) || plan_z(PLAN) % 2 == 0, "Z slices come in pairs (one unit each)");
   typedef typename Elem16<E>::v8 ev8;
   typedef typename Elem16<E>::v4 ev4;
   typedef typename Elem16<E>::v2 ev2;
@@ -432,8 +468,10 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_h16(FwdArgs a) {
   RowState st;
   const float c = a.c, tau = a.tau;
   f32x16 oacc[NMT];
-  float lsum;       // row sum of the rounded P~ (VALU; this lane's keys only)
-  f32x16 lacc;      // the same on the MFMA (every register holds the full sum)
+  float lsum;       // row sum of the rounded P~ over the steps the vector unit
+                    // takes (this lane's keys only)
+  f32x16 lacc;      // the same over the matrix unit's steps (every register
+                    // holds the full sum)
   float lexact;     // row sum of the unrounded P~ (this lane's keys only)
   // Pipeline registers: entering step j, S_j in S[0] and P~_{j-1} in P[1]
   // (the steady steps alternate the two sets)
@@ -467,8 +505,8 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_h16(FwdArgs a) {
   };
   auto pv_mfma = [&](int i, ev8 av, const ev8* pk) {
     oacc[i % NMT] = Elem16<E>::mfma(av, pk[i / NMT], oacc[i % NMT]);
-    if constexpr (ROWSUM_MFMA)   // step 7 on the matrix unit: ones x P~^T
-      if (i % NMT == NMT - 1)
+    if constexpr (ROWSUM_ANY)   // step 7 on the matrix unit: ones x P~^T
+      if (i % NMT == NMT - 1 && rs_on_mfma(PLAN, i / NMT))
         lacc = Elem16<E>::mfma(ones, pk[i / NMT], lacc);
   };
   auto qk = [&](int slot, f32x16& t0, f32x16& t1) {
@@ -577,6 +615,47 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_h16(FwdArgs a) {
     uz[k][0] = __builtin_fmaf(sv[r], c, nb);
     uz[k][1] = __builtin_fmaf(sv[r + 1], c, nb);
   };
+  // Z on the matrix unit (the plan's slices, steady steps only: the S of a
+  // steady step holds no masked -inf logit, which a zero of the selection
+  // operand would turn into NaN).  Per 32x32 tile, one chain of f32 products
+  // into zacc[t]: first the offset (lane half 0 passes 1 against -c*ref, half
+  // 1 passes 0, so every row of column n gets -c*ref of query n), then slice s
+  // as the B operand against c times the columns of I that pick its rows
+  // (rows 8(s/4) + 4h + s%4 of lane half h), the selection precomputed once.
+  f32x16 zacc[2];
+  float zsel[16];
+#pragma unroll
+  for (int sl = 0; sl < 16; ++sl)
+    zsel[sl] = (Z_ANY && (z_on_mfma(PLAN, 0, sl) || z_on_mfma(PLAN, 1, sl)) &&
+                ln == 8 * (sl / 4) + 4 * hf + sl % 4) ? c : 0.0f;
+  const float zoff_sel = hf == 0 ? 1.0f : 0.0f;
+  auto z_chain = [&](const f32x16& s0, const f32x16& s1, float nb) {
+    if constexpr (Z_ANY) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        bool any = false;
+#pragma unroll
+        for (int sl = 0; sl < 16; ++sl) any = any || z_on_mfma(PLAN, t, sl);
+        if (!any) continue;
+        const f32x16& sv = t ? s1 : s0;
+        f32x16 z = __builtin_amdgcn_mfma_f32_32x32x2f32(zoff_sel, nb, f32x16{}, 0, 0, 0);
+#pragma unroll
+        for (int sl = 0; sl < 16; ++sl)
+          if (z_on_mfma(PLAN, t, sl)) z = __builtin_amdgcn_mfma_f32_32x32x2f32(zsel[sl], sv[sl], z, 0, 0, 0);
+        zacc[t] = z;
+      }
+    }
+  };
+  // stage 1 in a steady step: the plan's slices come from the chain
+  auto unit_fma_steady = [&](int k, const f32x16& s0, const f32x16& s1, float nb) {
+    const int t = k / 8, r = 2 * (k % 8);
+    if (z_on_mfma(PLAN, t, r)) {
+      uz[k][0] = zacc[t][r];
+      uz[k][1] = zacc[t][r + 1];
+    } else {
+      unit_fma(k, s0, s1, nb);
+    }
+  };
   auto unit_exp = [&](int k) {
     up[k][0] = __builtin_amdgcn_exp2f(uz[k][0]);
     up[k][1] = __builtin_amdgcn_exp2f(uz[k][1]);
@@ -591,7 +670,7 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_h16(FwdArgs a) {
     w[1] = (E)p1;
     pk[2 * t + r / 8][r % 8] = w[0];
     pk[2 * t + r / 8][r % 8 + 1] = w[1];
-    if constexpr (!ROWSUM_MFMA) ps[t] = Elem16<E>::dot2(w, ones2, ps[t]);
+    if (!rs_on_mfma(PLAN, 2 * t + r / 8)) ps[t] = Elem16<E>::dot2(w, ones2, ps[t]);
   };
   auto exp_unit = [&](int k, const f32x16& s0, const f32x16& s1, ev8* pk, float nb) {
     unit_fma(k, s0, s1, nb);
@@ -602,36 +681,39 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_h16(FwdArgs a) {
   // MFMA row sum get alpha at the end of the step)
   auto sums_commit = [&](float alpha) {
     lexact = lexact * alpha + (pe[0] + pe[1]);
-    if constexpr (!ROWSUM_MFMA) lsum = lsum * alpha + (ps[0] + ps[1]);
+    if constexpr (!ROWSUM_ALL) lsum = lsum * alpha + (ps[0] + ps[1]);
   };
   // alpha on the matrix accumulators; the whole wave skips it when no row's
   // reference moved (alpha == 1 everywhere, the common case)
   auto rescale = [&](float alpha) {
     if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
-      if constexpr (SCALE_MFMA) {
-        // The repurposed-MMA scaling of FlashAttention-T (section A2, Fig 5(a))
-        // in fp32: O^T <- (alpha I) O^T as sixteen 32x32x2 f32 products per
-        // 32x32 tile.  Slice s pairs accumulator register s of the two lane
-        // halves (rows 8(s/4) + 4h + s%4, h = 0, 1) as the B operand with the
-        // matching columns of alpha I as the A operand.  alpha is the same in
-        // every lane here (one X = 32 tile per wave, no per-row fallback).
-        const int m = lane & 31, h = lane >> 5;
 #pragma unroll
-        for (int mt = 0; mt < NMT; ++mt) {
+      for (int mt = 0; mt < NMT; ++mt) {
+        bool any = false;
+#pragma unroll
+        for (int sl = 0; sl < 16; ++sl) any = any || (O_ANY && o_on_mfma(PLAN, mt, sl));
+        if (any) {
+          // The repurposed-MMA scaling of FlashAttention-T (section A2,
+          // Fig 5(a)) in fp32: O^T <- (alpha I) O^T as 32x32x2 f32 products.
+          // Slice s pairs accumulator register s of the two lane halves (rows
+          // 8(s/4) + 4h + s%4, h = 0, 1) as the B operand with the matching
+          // columns of alpha I as the A operand.  alpha is the same in every
+          // lane here (one X = 32 tile per wave, no per-row fallback).
           f32x16 dacc = {};
 #pragma unroll
           for (int sl = 0; sl < 16; ++sl) {
-            const float av = (m == 8 * (sl / 4) + 4 * h + sl % 4) ? alpha : 0.0f;
+            if (!o_on_mfma(PLAN, mt, sl)) continue;
+            const float av = (ln == 8 * (sl / 4) + 4 * hf + sl % 4) ? alpha : 0.0f;
             dacc = __builtin_amdgcn_mfma_f32_32x32x2f32(av, oacc[mt][sl], dacc, 0, 0, 0);
           }
-          oacc[mt] = dacc;
-          __builtin_amdgcn_sched_barrier(0);   // one tile's products at a time
-        }
-      } else {
 #pragma unroll
-        for (int mt = 0; mt < NMT; ++mt) oacc[mt] *= alpha;
+          for (int sl = 0; sl < 16; ++sl) oacc[mt][sl] = o_on_mfma(PLAN, mt, sl) ? dacc[sl] : oacc[mt][sl] * alpha;
+          __builtin_amdgcn_sched_barrier(0);   // one tile's products at a time
+        } else {
+          oacc[mt] *= alpha;
+        }
       }
-      if constexpr (ROWSUM_MFMA) lacc *= alpha;
+      if constexpr (ROWSUM_ANY) lacc *= alpha;
     }
   };
   auto step_loads = [&](int j, auto XING) {
@@ -698,10 +780,11 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_h16(FwdArgs a) {
   };
   // the unit stages that fall in chunk g (in stage order for each unit)
   auto unit_stages = [&](int g, const f32x16& c0, const f32x16& c1, ev8* pk, float nb) {
+    if (Z_ANY && g == MAXC) z_chain(c0, c1, nb);   // nb is known from here on
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
       const int uc = unit_chunk(k);
-      if (uc == g) unit_fma(k, c0, c1, nb);
+      if (uc == g) unit_fma_steady(k, c0, c1, nb);
       if (min(uc + SKEW, LASTC) == g) unit_exp(k);
       if (min(uc + 2 * SKEW, LASTC) == g) unit_sum_pack(k, pk);
     }
@@ -765,7 +848,7 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_h16(FwdArgs a) {
     pin(P[cur][2]);
     pin(P[cur][3]);
     pin(lexact);
-    if constexpr (!ROWSUM_MFMA) pin(lsum);
+    if constexpr (!ROWSUM_ALL) pin(lsum);
     step_barrier<2 * NV_STEP>();
     rescale(alpha);
   };
@@ -785,11 +868,9 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_h16(FwdArgs a) {
   int o_nrows = 0;          // its rows below N (uniform)
   float lse_out = 0.0f;
   auto finish = [&]() {
-    float l;
-    if constexpr (ROWSUM_MFMA)
-      l = lacc[0];
-    else
-      l = pair_reduce(lsum, [](float x, float y) { return x + y; });
+    float l = 0.0f;
+    if constexpr (ROWSUM_ANY) l = lacc[0];
+    if constexpr (!ROWSUM_ALL) l += pair_reduce(lsum, [](float x, float y) { return x + y; });
     const float le = pair_reduce(lexact, [](float x, float y) { return x + y; });
     const float inv = l > 0.0f ? a.o_scale / l : 0.0f;
     // (the lane's row, opaque here: its addresses are formed here, not

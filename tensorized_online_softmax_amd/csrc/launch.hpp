@@ -11,11 +11,11 @@ namespace tos {
 struct KernelChoice {
   int d;             // 64 or 128
   bool causal;
-  int x;             // 1, 16 or 32
-  bool rowsum_mfma;  // row sum on the matrix unit (fp8: always)
+  int x;             // 1, 16, 32 or 64
+  int plan = 0;      // split plan (split_plan in attn_fwd_kernels.hpp): 16-bit
+                     // kernels; fp8 always sums on the matrix unit, fp32 never
   bool fb_auto;      // fallback AUTO (x > 1 only)
-  bool seq = false;  // sequential schedule (16-bit kernels, x = 1 or 32, VALU row sum, no AUTO)
-  bool scale_mfma = false;   // O rescale on the matrix unit (16-bit kernels, x = 32, no fallback)
+  bool seq = false;  // sequential schedule (16-bit kernels, x = 1 or 32, vector row sum, no AUTO)
 };
 
 // Workgroups of a persistent launch over `nitems` items: one per compute unit

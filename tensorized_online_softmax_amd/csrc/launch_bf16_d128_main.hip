@@ -1,0 +1,7 @@
+// launch_bf16_d128_main.hip -- the 16-bit forward kernel's main instances for bfloat16 inputs, head dim 128.
+#define TOS_H16_DEFINE
+#include "launch_h16.hpp"
+
+namespace tos {
+template hipError_t H16<__bf16, 128>::main(const FwdArgs&, const KernelChoice&, hipStream_t);
+}  // namespace tos

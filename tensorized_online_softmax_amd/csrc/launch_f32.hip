@@ -16,7 +16,7 @@ static hipError_t go(const FwdArgs& a, hipStream_t s) {
 
 template <int D, bool CAUSAL>
 static hipError_t by_x(const FwdArgs& a, const KernelChoice& k, hipStream_t s) {
-  if (k.rowsum_mfma) return hipErrorNotSupported;
+  if (k.plan != kPlanValu) return hipErrorNotSupported;
   if (k.x == 1) return k.fb_auto ? hipErrorNotSupported : go<D, CAUSAL, 1, false>(a, s);
   if (k.x == 16) return k.fb_auto ? go<D, CAUSAL, 16, true>(a, s) : go<D, CAUSAL, 16, false>(a, s);
   if (k.x == 32) return k.fb_auto ? go<D, CAUSAL, 32, true>(a, s) : go<D, CAUSAL, 32, false>(a, s);

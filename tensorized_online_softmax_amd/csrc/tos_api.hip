@@ -81,13 +81,17 @@ tos_status tos_attn_fwd(const void* q, const void* k, const void* v, void* o, fl
   }
   if (op.x_tile != 1 && op.x_tile != 16 && op.x_tile != 32 && op.x_tile != 64)
     return TOS_ERR_INVALID_ARG;
-  if (op.softmax_split != TOS_SPLIT_VALU && op.softmax_split != TOS_SPLIT_ROWSUM_MFMA &&
-      op.softmax_split != TOS_SPLIT_SCALE_MFMA)
+  if (op.softmax_split < TOS_SPLIT_VALU || op.softmax_split > TOS_SPLIT_ALL_MFMA)
+    return TOS_ERR_INVALID_ARG;
+  if (op.split_den < 0 || op.split_num < 0 || op.split_num > op.split_den ||
+      (op.split_den == 0 && op.split_num != 0))
     return TOS_ERR_INVALID_ARG;
   if (op.fallback != TOS_FALLBACK_OFF && op.fallback != TOS_FALLBACK_AUTO &&
       op.fallback != TOS_FALLBACK_FORCE)
     return TOS_ERR_INVALID_ARG;
-  if (!std::isfinite(op.fallback_tau) || op.fallback_tau < 0.0f) return TOS_ERR_INVALID_ARG;
+  // tau > 126 would let the switch's rescale exp2(c*(ref - m_i)) overflow fp32
+  if (!std::isfinite(op.fallback_tau) || op.fallback_tau < 0.0f || op.fallback_tau > 126.0f)
+    return TOS_ERR_INVALID_ARG;
   if (op.schedule != TOS_SCHEDULE_COSCHED && op.schedule != TOS_SCHEDULE_SEQUENTIAL)
     return TOS_ERR_INVALID_ARG;
 
@@ -128,23 +132,54 @@ tos_status tos_attn_fwd(const void* q, const void* k, const void* v, void* o, fl
   tos::KernelChoice kc;
   kc.d = (int)d;
   kc.causal = causal != 0;
-  kc.rowsum_mfma = op.softmax_split == TOS_SPLIT_ROWSUM_MFMA;
   kc.x = op.fallback == TOS_FALLBACK_FORCE ? 1 : op.x_tile;
   kc.fb_auto = op.fallback == TOS_FALLBACK_AUTO && op.x_tile > 1;
   kc.seq = op.schedule == TOS_SCHEDULE_SEQUENTIAL;
-  kc.scale_mfma = op.softmax_split == TOS_SPLIT_SCALE_MFMA;
-  // the O rescale on the matrix unit needs one uniform factor per wave: an
-  // X = 32 tile and no fallback, in the 16-bit kernels
-  if (kc.scale_mfma && ((dtype != TOS_BF16 && dtype != TOS_F16) || op.x_tile != 32 ||
-                        op.fallback != TOS_FALLBACK_OFF || kc.seq))
+  const bool h16 = dtype == TOS_BF16 || dtype == TOS_F16;
+  // the matrix unit's share in quarters (the row-sum steps of a key block)
+  const bool has_share = op.split_den > 0;
+  if (has_share && (4 * op.split_num) % op.split_den != 0) return TOS_ERR_UNSUPPORTED;
+  const int quarters = has_share ? 4 * op.split_num / op.split_den : -1;
+  // every plan but the vector row sum and the full matrix-unit row sum runs at
+  // X = 32 without fallback, co-scheduled, in the 16-bit kernels: the O rescale
+  // on the matrix unit needs one alpha per wave
+  const bool x32_plain = h16 && op.x_tile == 32 && op.fallback == TOS_FALLBACK_OFF && !kc.seq;
+  switch (op.softmax_split) {
+    case TOS_SPLIT_VALU:
+      if (has_share && quarters != 0) return TOS_ERR_INVALID_ARG;
+      kc.plan = tos::kPlanValu;
+      break;
+    case TOS_SPLIT_ROWSUM_MFMA: {
+      const int rs = has_share ? quarters : 4;
+      if (dtype == TOS_F32) return TOS_ERR_UNSUPPORTED;
+      if (dtype == TOS_FP8_E4M3 && rs != 4) return TOS_ERR_UNSUPPORTED;
+      if (rs > 0 && rs < 4 && !x32_plain) return TOS_ERR_UNSUPPORTED;
+      kc.plan = tos::split_plan(rs, 0, 0, false);
+      break;
+    }
+    case TOS_SPLIT_SCALE_MFMA:
+      if (!x32_plain || (has_share && quarters != 4)) return TOS_ERR_UNSUPPORTED;
+      kc.plan = tos::kPlanScaleMfma;
+      break;
+    case TOS_SPLIT_HSPLIT:
+      if (!x32_plain || !has_share || quarters < 1 || quarters > 3) return TOS_ERR_UNSUPPORTED;
+      kc.plan = tos::split_plan(quarters, 4 * quarters, 4 * quarters, false);
+      break;
+    case TOS_SPLIT_VSPLIT:
+      if (!x32_plain || !has_share || quarters != 2) return TOS_ERR_UNSUPPORTED;
+      kc.plan = tos::split_plan(2, 1, (int)d / 64, true);
+      break;
+    case TOS_SPLIT_ALL_MFMA:
+      if (!x32_plain || (has_share && quarters != 4)) return TOS_ERR_UNSUPPORTED;
+      kc.plan = tos::split_plan(4, 16, 16, false);
+      break;
+  }
+  // fp8 sums on the matrix unit whatever the option
+  if (dtype == TOS_FP8_E4M3) kc.plan = tos::kPlanValu;
+  if (kc.seq && (!h16 || kc.plan != tos::kPlanValu || kc.fb_auto || kc.x == 16 || kc.x == 64))
     return TOS_ERR_UNSUPPORTED;
-  if (dtype == TOS_F32 && kc.rowsum_mfma) return TOS_ERR_UNSUPPORTED;
-  if (kc.seq && ((dtype != TOS_BF16 && dtype != TOS_F16) || kc.rowsum_mfma || kc.fb_auto ||
-                 kc.x == 16 || kc.x == 64))
-    return TOS_ERR_UNSUPPORTED;
-  // X = 64 (tiles of two waves): the 16-bit kernels with the VALU row sum
-  if (kc.x == 64 && ((dtype != TOS_BF16 && dtype != TOS_F16) || kc.rowsum_mfma))
-    return TOS_ERR_UNSUPPORTED;
+  // X = 64 (tiles of two waves): the 16-bit kernels with the vector row sum
+  if (kc.x == 64 && (!h16 || kc.plan != tos::kPlanValu)) return TOS_ERR_UNSUPPORTED;
 
   tos::FwdArgs a;
   a.q = q;
@@ -182,9 +217,9 @@ tos_status tos_attn_fwd(const void* q, const void* k, const void* v, void* o, fl
   else
     e = tos::launch_fp8(a, kc, s);
   if (log_enabled())
-    std::fprintf(stderr, "[tos] dtype=%d B=%lld H=%lld N=%lld d=%d causal=%d X=%d rowsum_mfma=%d "
+    std::fprintf(stderr, "[tos] dtype=%d B=%lld H=%lld N=%lld d=%d causal=%d X=%d plan=0x%x "
                  "fallback=%d sequential=%d items=%lld: %s\n", (int)dtype, (long long)B, (long long)H,
-                 (long long)N, kc.d, (int)kc.causal, kc.x, (int)kc.rowsum_mfma, op.fallback,
+                 (long long)N, kc.d, (int)kc.causal, kc.x, kc.plan, op.fallback,
                  (int)kc.seq, (long long)(BH * nqb), hipGetErrorString(e));
   if (e == hipErrorNotSupported) return TOS_ERR_UNSUPPORTED;
   return e == hipSuccess ? TOS_OK : TOS_ERR_HIP;

@@ -79,16 +79,3 @@ def assert_close(o, o_ref, lse, lse_ref, dtype, what="", storage_ulp=False):
     assert mean <= tmean, f"{what}: O mean {mean:.3e} (tol {tmean})"
     assert lrel <= TOL_LSE_REL, f"{what}: lse rel err {lrel:.3e}"
     return mx, mean, lrel
-
-
-def sample_rows(BH, N, n, seed, causal):
-    """Row indices (flat bh*N + i) covering the first, last and diagonal-edge
-    rows of every head plus random ones."""
-    rng = np.random.default_rng(seed)
-    rows = set()
-    for bh in range(BH):
-        for i in (0, 1, 31, 32, 63, 64, 127, 128, N // 2, N - 2, N - 1):
-            if 0 <= i < N:
-                rows.add(bh * N + i)
-    rows.update(int(x) for x in rng.integers(0, BH * N, size=n))
-    return np.array(sorted(rows), dtype=np.int64)

@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_helpers():
-    assert tb.tos_version() == 1
+    assert tb.tos_version() == 2
     assert tb.tos_attn_fwd_flops(2, 32, 4096, 128, 1) == 4.0 * 2 * 32 * 4096 ** 2 * 128 / 2
     assert tb.tos_attn_fwd_flops(4, 16, 1024, 64, 0) == 4.0 * 4 * 16 * 1024 ** 2 * 64
     assert tb.tos_attn_fwd_flops(0, 16, 1024, 64, 0) == 0.0
@@ -91,7 +91,6 @@ def opts(**kw):
     (dict(dtype=tb.TOS_FP8_E4M3, opts=opts(x_tile=64)), tb.TOS_ERR_UNSUPPORTED),
     (dict(opts=opts(x_tile=64, softmax_split=1)), tb.TOS_ERR_UNSUPPORTED),
     (dict(opts=opts(x_tile=64, schedule=1)), tb.TOS_ERR_UNSUPPORTED),
-    (dict(opts=opts(softmax_split=5)), tb.TOS_ERR_INVALID_ARG),
     (dict(dtype=tb.TOS_F32, opts=opts(softmax_split=2)), tb.TOS_ERR_UNSUPPORTED),
     (dict(dtype=tb.TOS_FP8_E4M3, opts=opts(softmax_split=2)), tb.TOS_ERR_UNSUPPORTED),
     (dict(opts=opts(softmax_split=2, x_tile=16)), tb.TOS_ERR_UNSUPPORTED),
@@ -112,6 +111,29 @@ def opts(**kw):
     (dict(opts=opts(schedule=1, x_tile=16)), tb.TOS_ERR_UNSUPPORTED),
     (dict(opts=opts(schedule=1, fallback=1)), tb.TOS_ERR_UNSUPPORTED),
     (dict(dtype=4), tb.TOS_ERR_INVALID_ARG),
+    # tau above 126: the switch's rescale by up to 2^tau would overflow fp32
+    (dict(opts=opts(fallback=1, fallback_tau=127.0)), tb.TOS_ERR_INVALID_ARG),
+    (dict(opts=opts(fallback=1, fallback_tau=float("inf"))), tb.TOS_ERR_INVALID_ARG),
+    # split values and shares
+    (dict(opts=opts(softmax_split=6)), tb.TOS_ERR_INVALID_ARG),
+    (dict(opts=opts(softmax_split=-1)), tb.TOS_ERR_INVALID_ARG),
+    (dict(opts=opts(softmax_split=1, split_num=3, split_den=2)), tb.TOS_ERR_INVALID_ARG),
+    (dict(opts=opts(softmax_split=1, split_num=1, split_den=0)), tb.TOS_ERR_INVALID_ARG),
+    (dict(opts=opts(softmax_split=1, split_num=-1, split_den=4)), tb.TOS_ERR_INVALID_ARG),
+    (dict(opts=opts(softmax_split=0, split_num=1, split_den=2)), tb.TOS_ERR_INVALID_ARG),
+    (dict(opts=opts(softmax_split=1, split_num=1, split_den=3)), tb.TOS_ERR_UNSUPPORTED),
+    (dict(opts=opts(softmax_split=3)), tb.TOS_ERR_UNSUPPORTED),          # HSPLIT needs a share
+    (dict(opts=opts(softmax_split=3, split_num=1, split_den=1)), tb.TOS_ERR_UNSUPPORTED),
+    (dict(opts=opts(softmax_split=4, split_num=1, split_den=4)), tb.TOS_ERR_UNSUPPORTED),
+    (dict(opts=opts(softmax_split=1, split_num=1, split_den=2, x_tile=16)), tb.TOS_ERR_UNSUPPORTED),
+    (dict(opts=opts(softmax_split=1, split_num=1, split_den=2, fallback=1)), tb.TOS_ERR_UNSUPPORTED),
+    (dict(opts=opts(softmax_split=3, split_num=1, split_den=2, fallback=2)), tb.TOS_ERR_UNSUPPORTED),
+    (dict(opts=opts(softmax_split=5, schedule=1)), tb.TOS_ERR_UNSUPPORTED),
+    (dict(dtype=tb.TOS_F32, opts=opts(softmax_split=5)), tb.TOS_ERR_UNSUPPORTED),
+    (dict(dtype=tb.TOS_FP8_E4M3, opts=opts(softmax_split=3, split_num=1, split_den=2)),
+     tb.TOS_ERR_UNSUPPORTED),
+    (dict(dtype=tb.TOS_FP8_E4M3, opts=opts(softmax_split=1, split_num=1, split_den=2)),
+     tb.TOS_ERR_UNSUPPORTED),
     (dict(B=70000, H=70000), tb.TOS_ERR_UNSUPPORTED),       # grid beyond 2^31
     # empty problems: nothing to do, and no pointer is needed
     (dict(B=0, q=None, k=None, v=None, o=None), tb.TOS_OK),
@@ -120,3 +142,47 @@ def opts(**kw):
 ])
 def test_validation(kw, status):
     assert call(**kw) == status
+
+
+# ---- the Python binding's tensor checks (CPU tensors: every check below fires
+# before the library is called)
+
+def _t(shape=(1, 2, 8, 64), dtype=None, **kw):
+    import torch
+    return torch.zeros(shape, dtype=dtype or torch.bfloat16, **kw)
+
+
+def test_binding_rejects_bad_tensors():
+    import torch
+    q = _t()
+    good = dict(q=q, k=_t(), v=_t())
+    with pytest.raises(ValueError, match="4-D"):
+        tb.check_tensors(_t((2, 8, 64)), _t(), _t())
+    with pytest.raises(ValueError, match="shapes differ"):
+        tb.check_tensors(q, _t((1, 2, 9, 64)), _t())
+    with pytest.raises(ValueError, match="needs"):
+        tb.check_tensors(q, _t(), _t(), dtype="f32")            # bf16 data, f32 named
+    with pytest.raises(ValueError, match="needs"):
+        tb.check_tensors(q, _t(dtype=torch.float16), _t())      # mixed input dtypes
+    with pytest.raises(ValueError, match="contiguous"):
+        tb.check_tensors(_t((1, 8, 2, 64)).transpose(1, 2), _t(), _t())
+    with pytest.raises(ValueError, match="out must be"):
+        tb.check_tensors(**good, out=_t((1, 2, 8, 32)))          # undersized out
+    with pytest.raises(ValueError, match="out must be"):
+        tb.check_tensors(**good, out=_t(dtype=torch.float32))   # wrong O dtype
+    with pytest.raises(ValueError, match="lse must be"):
+        tb.check_tensors(**good, lse=torch.zeros(1, 2, 7))
+    with pytest.raises(ValueError, match="lse must be"):
+        tb.check_tensors(**good, lse=torch.zeros(1, 2, 8, dtype=torch.float64))
+    with pytest.raises(ValueError, match="fallback_tiles"):
+        tb.check_tensors(**good, fallback_tiles=torch.zeros(1, dtype=torch.int64))
+    with pytest.raises(ValueError, match="unsupported input dtype"):
+        tb.check_tensors(_t(dtype=torch.float64), _t(dtype=torch.float64), _t(dtype=torch.float64))
+    # everything well formed but on the CPU: rejected as not being on the GPU
+    with pytest.raises(ValueError, match="CUDA"):
+        tb.check_tensors(**good, out=_t(), lse=torch.zeros(1, 2, 8))
+    # attn_fwd runs the same checks before it allocates or launches
+    with pytest.raises(ValueError, match="needs"):
+        tb.attn_fwd(q, _t(), _t(), dtype="f16")
+    with pytest.raises(ValueError, match="CUDA"):
+        tb.attn_fwd(q, _t(), _t())
