@@ -174,6 +174,10 @@ __device__ __forceinline__ void count_tiles(const FwdArgs& a, const RowState& st
 // slots are constants folded into the LDS instructions, and S and P~ alternate
 // between two register sets instead of being copied.
 // ---------------------------------------------------------------------------
+#ifndef TOS_STEADY_EXACT_SUM
+#define TOS_STEADY_EXACT_SUM 1
+#endif
+
 constexpr int kPWaves = 8;
 constexpr int kPThreads = 64 * kPWaves;
 constexpr int kPBr = 32 * kPWaves;   // 256 query rows per workgroup
@@ -660,7 +664,19 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_h16(FwdArgs a) {
     up[k][0] = __builtin_amdgcn_exp2f(uz[k][0]);
     up[k][1] = __builtin_amdgcn_exp2f(uz[k][1]);
   };
-  auto unit_sum_pack = [&](int k, ev8* pk) {
+  // The rounded row sum (the normaliser of O) is taken on the vector unit only
+  // in a wave's edge steps (its first and last key blocks, and the idle steps of
+  // a causal item); a steady step adds its unrounded sum instead.  A row whose
+  // keys are few (the early rows of a causal head) has all of them in edge
+  // blocks, where O / l must stay an exact weighted average of V rows; a row
+  // with steady blocks has more than 128 keys, over which the 16-bit rounding
+  // of P~ averages out.  This drops the dot products (which wait for the
+  // matrix unit to go idle) from the steady steps.  bf16 only: its P~ keeps
+  // fp32's exponent range, while fp16 P~ flushes rows far below their tile's
+  // surrogate, and there an unrounded sum next to a flushed numerator would
+  // shrink O towards 0 instead of leaving the surviving terms' average.
+  constexpr bool STEADY_EXACT = TOS_STEADY_EXACT_SUM && PLAN == kPlanValu && Elem16<E>::kPreLog2 == 0;
+  auto unit_sum_pack = [&](int k, ev8* pk, bool steady) {
     const int t = k / 8, r = 2 * (k % 8);
     const float p0 = up[k][0], p1 = up[k][1];
     pe[t] += p0;
@@ -670,18 +686,20 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_h16(FwdArgs a) {
     w[1] = (E)p1;
     pk[2 * t + r / 8][r % 8] = w[0];
     pk[2 * t + r / 8][r % 8 + 1] = w[1];
-    if (!rs_on_mfma(PLAN, 2 * t + r / 8)) ps[t] = Elem16<E>::dot2(w, ones2, ps[t]);
+    if (!(steady && STEADY_EXACT) && !rs_on_mfma(PLAN, 2 * t + r / 8))
+      ps[t] = Elem16<E>::dot2(w, ones2, ps[t]);
   };
   auto exp_unit = [&](int k, const f32x16& s0, const f32x16& s1, ev8* pk, float nb) {
     unit_fma(k, s0, s1, nb);
     unit_exp(k);
-    unit_sum_pack(k, pk);
+    unit_sum_pack(k, pk, false);
   };
   // the block's sums into the running ones (which absorb alpha here; O and the
   // MFMA row sum get alpha at the end of the step)
-  auto sums_commit = [&](float alpha) {
-    lexact = lexact * alpha + (pe[0] + pe[1]);
-    if constexpr (!ROWSUM_ALL) lsum = lsum * alpha + (ps[0] + ps[1]);
+  auto sums_commit = [&](float alpha, bool steady) {
+    const float e = pe[0] + pe[1];
+    lexact = lexact * alpha + e;
+    if constexpr (!ROWSUM_ALL) lsum = lsum * alpha + ((steady && STEADY_EXACT) ? e : ps[0] + ps[1]);
   };
   // alpha on the matrix accumulators; the whole wave skips it when no row's
   // reference moved (alpha == 1 everywhere, the common case)
@@ -744,7 +762,7 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_h16(FwdArgs a) {
       sums_reset();
 #pragma unroll
       for (int k = 0; k < 16; ++k) exp_unit(k, S[0][0], S[0][1], P[0], nb);
-      sums_commit(alpha);
+      sums_commit(alpha, false);
     }
     if (j + 1 < jend_w) qk((j + 1) % kRing, S[0][0], S[0][1]);
     if (j >= 1 && j <= jend_w) pv((j - 1) % kRing, P[1]);
@@ -786,7 +804,7 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_h16(FwdArgs a) {
       const int uc = unit_chunk(k);
       if (uc == g) unit_fma_steady(k, c0, c1, nb);
       if (min(uc + SKEW, LASTC) == g) unit_exp(k);
-      if (min(uc + 2 * SKEW, LASTC) == g) unit_sum_pack(k, pk);
+      if (min(uc + 2 * SKEW, LASTC) == g) unit_sum_pack(k, pk, true);
     }
   };
   auto max_chunk = [&](int i, f32x16& c0, f32x16& c1, float& alpha, float& nb) {
@@ -842,7 +860,7 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_h16(FwdArgs a) {
       unit_stages(NQK + i, c0, c1, P[cur], nb);
       __builtin_amdgcn_sched_barrier(0);
     }
-    sums_commit(alpha);
+    sums_commit(alpha, true);
     pin(P[cur][0]);
     pin(P[cur][1]);
     pin(P[cur][2]);

@@ -52,28 +52,40 @@ def errors(o, o_ref, lse, lse_ref):
     return float(e.max()), float(e.mean()), float(el.max())
 
 
-def bf16_ulp(x):
-    """Spacing of bfloat16 numbers at |x| (8 significant bits)."""
-    ax = np.maximum(np.abs(x), 2.0 ** -126)
-    return 2.0 ** (np.floor(np.log2(ax)) - 7)
+def storage_ulp(x, dtype):
+    """Spacing of the output type's numbers at |x|: bf16 (8 significant bits)
+    or fp16 (11 significant bits, subnormal spacing 2^-24)."""
+    ax = np.abs(x)
+    if dtype == "f16":
+        return 2.0 ** (np.floor(np.log2(np.maximum(ax, 2.0 ** -14))) - 10)
+    return 2.0 ** (np.floor(np.log2(np.maximum(ax, 2.0 ** -126))) - 7)
 
 
-def assert_close(o, o_ref, lse, lse_ref, dtype, what="", storage_ulp=False):
+def round_to_output(x, dtype):
+    t = torch.from_numpy(np.ascontiguousarray(x))
+    return t.to(torch.float16 if dtype == "f16" else torch.bfloat16).double().numpy()
+
+
+def assert_close(o, o_ref, lse, lse_ref, dtype, what="", storage_ulp_rule=True, **_):
     """Max and mean abs error of O within TOL_O[dtype], lse within 1e-3 relative.
 
-    storage_ulp (bf16 output only): an element whose error exceeds the max
-    tolerance still passes when it is within one bf16 ulp of the oracle value
-    rounded to bf16 -- the storage rounding of |O| >= 2 alone can reach 2^-8
-    (used for peaked stress inputs whose rows average only a few keys).
+    16-bit outputs (bf16 for bf16 and fp8 inputs, fp16 for fp16): an element whose
+    error exceeds the max bound still passes when it is within one unit of the
+    output type of the oracle value rounded to that type -- storing |O| >= 2 in
+    bf16 alone can be off by 2^-8 (half its spacing there), beyond 1e-2 once the
+    computation's own error is added, so the bound cannot be met element by
+    element in early causal rows, which average only a few values of V.
     """
     assert np.all(np.isfinite(o)), f"{what}: non-finite O"
     assert np.all(np.isfinite(lse)), f"{what}: non-finite lse"
     mx, mean, lrel = errors(o, o_ref, lse, lse_ref)
     tmax, tmean = TOL_O[dtype]
-    if storage_ulp and mx > tmax:
-        ref16 = torch.from_numpy(np.ascontiguousarray(o_ref)).to(torch.bfloat16).double().numpy()
-        bad = (np.abs(o - o_ref) > tmax) & (np.abs(o - ref16) > bf16_ulp(ref16))
-        assert not bad.any(), f"{what}: {bad.sum()} elements beyond 1e-2 and 1 bf16 ulp"
+    if storage_ulp_rule and dtype != "f32" and mx > tmax:
+        out = "f16" if dtype == "f16" else "bf16"
+        ref16 = round_to_output(o_ref, out)
+        bad = (np.abs(o - o_ref) > tmax) & (np.abs(o - ref16) > storage_ulp(ref16, out))
+        assert not bad.any(), (f"{what}: {bad.sum()} elements beyond {tmax} and 1 {out} unit "
+                               f"(max {mx:.3e})")
     else:
         assert mx <= tmax, f"{what}: O max {mx:.3e} (tol {tmax})"
     assert mean <= tmean, f"{what}: O mean {mean:.3e} (tol {tmean})"

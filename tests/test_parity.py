@@ -141,7 +141,7 @@ def test_fallback_auto_switches_on_spiky_rows():
     for fb, tau in (("off", 0.0), ("auto", 12.0), ("auto", 0.0)):
         o, lse, tiles = run_gpu(inp, False, fallback=fb, tau=tau, counter=True)
         assert_close(o.reshape(o_ref.shape), o_ref, lse.reshape(lse_ref.shape), lse_ref,
-                     "bf16", f"spiky fallback={fb} tau={tau}", storage_ulp=True)
+                     "bf16", f"spiky fallback={fb} tau={tau}")
         if fb == "auto" and tau == 12.0:
             assert tiles > 0
         if fb == "off" or tau == 0.0:
@@ -369,7 +369,7 @@ def test_x64_fallback_counts_tiles():
     o_ref, lse_ref = oracle_exact(inp, False)
     o, lse, tiles = run_gpu(inp, False, x_tile=64, fallback="auto", tau=12.0, counter=True)
     assert_close(o.reshape(o_ref.shape), o_ref, lse.reshape(lse_ref.shape), lse_ref, "bf16",
-                 "X=64 spiky AUTO", storage_ulp=True)
+                 "X=64 spiky AUTO")
     q, k, v = real_inputs(inp)
     model = oracle.attn_surrogate(q, k, v, False, inp["scale"], X=64, Bc=64, fallback=1,
                                   tau=12.0)
