@@ -26,7 +26,9 @@
 //     instructions cost little.
 //   * The row sum that normalises O is the sum of hi + lo that the product
 //     consumes, taken on the matrix unit (an all-ones operand against each
-//     term); the unrounded fp32 sum gives lse.
+//     term) for the blocks of a wave's edge steps, and the unrounded fp32 sum
+//     for those of its steady steps (see steady_step); the unrounded fp32 sum
+//     of every block gives lse.
 //
 // Operand layouts (32x32x64 e4m3, measured on gfx950): slot t of lane half h
 // of the A operand meets slot t of lane half h of the B operand.  So, as in
@@ -206,7 +208,10 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_fp8(FwdArgs a) {
   RowState st;
   const float c = a.c, tau = a.tau;
   f32x16 oacc[NMT];
-  f32x16 lacc;      // row sum of hi + lo of 2^8 P~ (MFMA; every register holds it)
+  f32x16 lacc;      // row sum of hi + lo of 2^8 P~ over the edge steps (MFMA;
+                    // every register holds it)
+  float lsteady;    // row sum of the unrounded 2^8 P~ over the steady steps
+                    // (this lane's keys only)
   float lexact;     // row sum of the unrounded 2^8 P~ (this lane's keys only)
   // pipeline registers: entering step j, S_j in S[0] and the hi and lo terms
   // of P~_{j-1} in PH[1], PL[1] (the steady steps alternate the two sets)
@@ -244,7 +249,7 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_fp8(FwdArgs a) {
       s1 = mfma_f8(kread(slot, 1, kk), qf[kk], s1);
     }
   };
-  // O^T += V_j^T (hi + lo)^T, and the row sum of hi + lo (ones x (hi + lo)^T)
+  // O^T += V_j^T (hi + lo)^T
   auto pv = [&](int slot, const i32x8& hi, const i32x8& lo) {
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt) {
@@ -252,8 +257,6 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_fp8(FwdArgs a) {
       oacc[mt] = mfma_f8(vop, hi, oacc[mt]);
       oacc[mt] = mfma_f8(vop, lo, oacc[mt]);
     }
-    lacc = mfma_f8(ones, hi, lacc);
-    lacc = mfma_f8(ones, lo, lacc);
   };
 
   // ---- the softmax of one key block (Algorithm 1), in pieces
@@ -359,11 +362,18 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_fp8(FwdArgs a) {
 #pragma unroll
       for (int k = 0; k < 8; ++k) exp_unit(k, S[0][0], S[0][1], PH[0], PL[0], nb);
       lexact = lexact * alpha + (pe[0] + pe[1]);
+      lsteady *= alpha;
     }
     if (j + 1 < jend_w) qk((j + 1) % kRing, S[0][0], S[0][1]);
     if (j >= 1 && j <= jend_w) pv((j - 1) % kRing, PH[1], PL[1]);
     step_barrier<2 * NV_STEP>();
-    if (j < jend_w) rescale(alpha);
+    if (j < jend_w) {
+      rescale(alpha);
+      // this block's rounded row sum (ones x (hi + lo)^T), after the rescale:
+      // its terms are relative to the new reference already
+      lacc = mfma_f8(ones, PH[0], lacc);
+      lacc = mfma_f8(ones, PL[0], lacc);
+    }
     PH[1] = PH[0];
     PL[1] = PL[0];
   };
@@ -372,8 +382,14 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_fp8(FwdArgs a) {
   // One straight-line block of matrix-instruction chunks:
   //   A (4 chunks): S_{j+1} = K_{j+1} Q^T, each with a part of the tile-maximum
   //                 chain of S_j (parts 0-1 | 2-3 | combine + tile max | advance)
-  //   B (10 chunks): O^T += V_{j-1}^T (hi + lo)^T and the row sum of P~_{j-1},
-  //                 with the 8 exponential units of S_j in the first 8
+  //   B (8 chunks): O^T += V_{j-1}^T (hi + lo)^T, with the 8 exponential units
+  //                 of S_j
+  // The rounded row sum (ones x (hi + lo)^T on the matrix unit) is taken for
+  // the blocks of the edge steps only (a wave's first and last key blocks,
+  // which hold every key of a row that has few); a steady step adds the
+  // unrounded sum of its block to O's normaliser instead (such a row has more
+  // than 128 keys, over which the rounding of hi + lo averages out), which
+  // saves two matrix instructions of 64 clocks per step.
   // Constant ring slots (four steps per loop iteration); S and P~ alternate
   // between the two register sets.
   auto steady_step = [&](auto U, int j, auto XING) {
@@ -411,39 +427,39 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_fp8(FwdArgs a) {
     }
     __builtin_amdgcn_s_setprio(0);
     // phase B: per M tile one V operand for the hi and the lo product
+    constexpr int NB = 2 * NMT;
     i32x8 vop = vread(vslot, 0), vop_hold = {};
 #pragma unroll
-    for (int i = 0; i < 2 * NMT + 2; ++i) {
-      if (i < 2 * NMT) {
-        const int mt = i / 2;
-        if (i % 2 == 0) {
-          const i32x8 av = vop;
-          if (mt + 1 < NMT) vop = vread(vslot, mt + 1);
-          oacc[mt] = mfma_f8(av, PH[nxt], oacc[mt]);
-          vop_hold = av;
-        } else {
-          oacc[mt] = mfma_f8(vop_hold, PL[nxt], oacc[mt]);
-        }
+    for (int i = 0; i < NB; ++i) {
+      const int mt = i / 2;
+      if (i % 2 == 0) {
+        const i32x8 av = vop;
+        if (mt + 1 < NMT) vop = vread(vslot, mt + 1);
+        oacc[mt] = mfma_f8(av, PH[nxt], oacc[mt]);
+        vop_hold = av;
       } else {
-        lacc = mfma_f8(ones, i == 2 * NMT ? PH[nxt] : PL[nxt], lacc);
+        oacc[mt] = mfma_f8(vop_hold, PL[nxt], oacc[mt]);
       }
-      // the 8 exponential units: one per chunk at d = 128 (unit i's three
-      // stages in chunks i, i+1 and i+2), spread over the 6 chunks at d = 64
+      // the 8 exponential units: one per chunk at d = 128 (unit k's three
+      // stages in chunks k, k+1 and k+2, clamped to the last), spread over the
+      // 4 chunks at d = 64
       if constexpr (D == 128) {
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
           if (k == i) unit_fma(k, c0, c1, nb);
-          if (k + 1 == i) unit_exp(k);
-          if (k + 2 == i) unit_sum_pack(k, PH[cur], PL[cur]);
+          if (min(k + 1, NB - 1) == i) unit_exp(k);
+          if (min(k + 2, NB - 1) == i) unit_sum_pack(k, PH[cur], PL[cur]);
         }
       } else {
 #pragma unroll
         for (int k = 0; k < 8; ++k)
-          if (k * (2 * NMT + 2) / 8 == i) exp_unit(k, c0, c1, PH[cur], PL[cur], nb);
+          if (k * NB / 8 == i) exp_unit(k, c0, c1, PH[cur], PL[cur], nb);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    lexact = lexact * alpha + (pe[0] + pe[1]);
+    const float e = pe[0] + pe[1];
+    lexact = lexact * alpha + e;
+    lsteady = lsteady * alpha + e;
     pin(PH[cur]);
     pin(PL[cur]);
     pin(lexact);
@@ -465,7 +481,7 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_fp8(FwdArgs a) {
   int o_nrows = 0;
   float lse_out = 0.0f;
   auto finish = [&]() {
-    const float l = lacc[0];
+    const float l = lacc[0] + pair_reduce(lsteady, [](float x, float y) { return x + y; });
     const float le = pair_reduce(lexact, [](float x, float y) { return x + y; });
     const float inv = l > 0.0f ? a.o_scale / l : 0.0f;
     int sr = ln;
@@ -522,6 +538,7 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_fp8(FwdArgs a) {
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt) oacc[mt] = f32x16{};
     lacc = f32x16{};
+    lsteady = 0.0f;
     lexact = 0.0f;
     S[0][0] = S[0][1] = S[1][0] = S[1][1] = f32x16{};
     PH[0] = PH[1] = PL[0] = PL[1] = i32x8{};

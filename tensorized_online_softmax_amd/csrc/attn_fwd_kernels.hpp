@@ -174,10 +174,6 @@ __device__ __forceinline__ void count_tiles(const FwdArgs& a, const RowState& st
 // slots are constants folded into the LDS instructions, and S and P~ alternate
 // between two register sets instead of being copied.
 // ---------------------------------------------------------------------------
-#ifndef TOS_STEADY_EXACT_SUM
-#define TOS_STEADY_EXACT_SUM 1
-#endif
-
 constexpr int kPWaves = 8;
 constexpr int kPThreads = 64 * kPWaves;
 constexpr int kPBr = 32 * kPWaves;   // 256 query rows per workgroup
@@ -601,6 +597,18 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_h16(FwdArgs a) {
     alpha = ref_advance(st, ref_new, c);
     nb = neg_c_ref(st, c) + (float)Elem16<E>::kPreLog2;
   };
+  // the same in a steady step of a wave-wide tile without fallback: every row of
+  // the wave has seen key block 0 by then, so the old and the new reference are
+  // finite and the guards of ref_advance / neg_c_ref are not needed
+  auto advance_steady = [&](float& alpha, float& nb) {
+    if constexpr (X == 32 && !FB_AUTO) {
+      alpha = __builtin_amdgcn_exp2f(c * (st.ref - ref_new));
+      st.ref = ref_new;
+      nb = __builtin_fmaf(-c, ref_new, (float)Elem16<E>::kPreLog2);
+    } else {
+      advance(alpha, nb);
+    }
+  };
   // steps 4-7 for registers r, r+1 of tile t (unit k: t = k / 8,
   // r = 2 (k % 8)): P~ = exp2(c*S - c*ref), packed to 16 bits as the B operand
   // of the P~V product, and both row sums.  The unrounded sum gives lse; the
@@ -675,7 +683,7 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_h16(FwdArgs a) {
   // fp32's exponent range, while fp16 P~ flushes rows far below their tile's
   // surrogate, and there an unrounded sum next to a flushed numerator would
   // shrink O towards 0 instead of leaving the surviving terms' average.
-  constexpr bool STEADY_EXACT = TOS_STEADY_EXACT_SUM && PLAN == kPlanValu && Elem16<E>::kPreLog2 == 0;
+  constexpr bool STEADY_EXACT = PLAN == kPlanValu && Elem16<E>::kPreLog2 == 0;
   auto unit_sum_pack = [&](int k, ev8* pk, bool steady) {
     const int t = k / 8, r = 2 * (k % 8);
     const float p0 = up[k][0], p1 = up[k][1];
@@ -783,14 +791,14 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_h16(FwdArgs a) {
   // The chain (d=128: parts 0-1 | 2-3 | combine | tile max | advance; d=64:
   // parts 0-3 | combine, tile max | advance) takes the first chunks of A;
   // units are spread evenly over the chunks after it and over B.  At d=128 a
-  // unit's three stages go to chunks c, c+2 and c+4 of the step (clamped to
+  // unit's three stages go to chunks c, c+1 and c+2 of the step (clamped to
   // its last chunk), so that no stage waits for the one before it.  Operand
   // reads run LA instructions ahead; S and P~ alternate between the two
   // register sets.
   constexpr int MAXC = NQK >= 16 ? 5 : 3;      // phase-A chunks of the maximum chain
   constexpr int EA = NQK >= 16 ? 6 : 3;        // exponential units in phase A
   constexpr int LA = 3;                        // operand read lookahead
-  constexpr int SKEW = NQK >= 16 ? 2 : 0;      // chunks between a unit's stages
+  constexpr int SKEW = NQK >= 16 ? 1 : 0;      // chunks between a unit's stages
   constexpr int LASTC = NQK + NPV - 1;         // last chunk of a step
   // chunk of unit k's first stage
   auto unit_chunk = [&](int k) -> int {
@@ -813,14 +821,14 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_h16(FwdArgs a) {
       if (i == 1) { max_part(2, c0, c1); max_part(3, c0, c1); }
       if (i == 2) max_combine();
       if (i == 3) tile_ref();
-      if (i == 4) advance(alpha, nb);
+      if (i == 4) advance_steady(alpha, nb);
     } else {
       if (i == 0) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) max_part(q, c0, c1);
       }
       if (i == 1) { max_combine(); tile_ref(); }
-      if (i == 2) advance(alpha, nb);
+      if (i == 2) advance_steady(alpha, nb);
     }
   };
   auto steady_step = [&](auto U, int j, auto XING) {
