@@ -25,6 +25,13 @@
  *     per-device record of the compute-unit count, read on the first call
  *     that launches on the device (the kernels run one workgroup per compute
  *     unit, each over a list of query blocks).
+ *   - Problems with fewer 256-row query blocks than the device has compute
+ *     units (few heads, short sequences) can also cut each query block's keys
+ *     into pieces that run on separate compute units and are merged by a
+ *     second kernel on the same stream.  That needs a device workspace from
+ *     the caller (tos_fwd_opts.workspace, sized by tos_attn_fwd_workspace_size);
+ *     without one the call runs whole query blocks, with the same results up
+ *     to rounding.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
  *     the call returns without synchronising.  A device fault surfaces at the
  *     caller's next synchronisation.
@@ -35,6 +42,7 @@
 #ifndef TOS_H
 #define TOS_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -152,6 +160,13 @@ typedef struct {
     int schedule;          /* a tos_schedule value                                  */
     int split_num;         /* the matrix unit's share split_num / split_den of the */
     int split_den;         /* softmax_split value (0 / 0: the value's default)     */
+    void* workspace;       /* NULL, or device memory of workspace_bytes that the
+                              bf16 / f16 kernels may use for pieces of query
+                              blocks (see the conventions above); used only when
+                              workspace_bytes >= tos_attn_fwd_workspace_size(...)
+                              and the fallback is off; must not overlap the
+                              tensors; its contents on entry do not matter      */
+    size_t workspace_bytes;
 } tos_fwd_opts;
 
 /*
@@ -179,8 +194,19 @@ tos_status tos_attn_fwd(const void* q, const void* k, const void* v, void* o, fl
                         int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
                         tos_dtype dtype, const tos_fwd_opts* opts, void* stream);
 
+/* Device workspace, in bytes, that tos_attn_fwd with these arguments and
+ * options (NULL = defaults) would use to cut query blocks into pieces on the
+ * current device: 0 when the problem has enough query blocks to fill the
+ * device, or the options rule it out (fp32 or fp8 inputs, a fallback other
+ * than off).  At most 256 x 256 x (d + 1) x 4 bytes (33.8 MB at d = 128).
+ * Returns TOS_ERR_INVALID_ARG for a NULL bytes pointer or sizes/options that
+ * tos_attn_fwd would reject as invalid. */
+tos_status tos_attn_fwd_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d, int causal,
+                                       tos_dtype dtype, const tos_fwd_opts* opts, size_t* bytes);
+
 /* Fills *opts with the defaults (size set, X = 32, VALU, fallback off,
- * descales 1, co-scheduled).  Returns TOS_ERR_INVALID_ARG for NULL. */
+ * descales 1, co-scheduled, no workspace).  Returns TOS_ERR_INVALID_ARG for
+ * NULL. */
 tos_status tos_fwd_opts_default(tos_fwd_opts* opts);
 
 /* Algorithmic matrix-unit work of one call: 4*B*H*N^2*d flops, halved when

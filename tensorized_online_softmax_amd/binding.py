@@ -19,7 +19,7 @@ TOS_FALLBACK_OFF, TOS_FALLBACK_AUTO, TOS_FALLBACK_FORCE = 0, 1, 2
 TOS_SCHEDULE_COSCHED, TOS_SCHEDULE_SEQUENTIAL = 0, 1
 
 EXPORTED = ("tos_attn_fwd", "tos_fwd_opts_default", "tos_attn_fwd_flops",
-            "tos_status_string", "tos_version")
+            "tos_attn_fwd_workspace_size", "tos_status_string", "tos_version")
 
 
 class tos_fwd_opts(ctypes.Structure):
@@ -28,7 +28,8 @@ class tos_fwd_opts(ctypes.Structure):
                 ("fallback_tau", ctypes.c_float), ("q_descale", ctypes.c_float),
                 ("k_descale", ctypes.c_float), ("v_descale", ctypes.c_float),
                 ("fallback_tiles", ctypes.c_void_p), ("schedule", ctypes.c_int),
-                ("split_num", ctypes.c_int), ("split_den", ctypes.c_int)]
+                ("split_num", ctypes.c_int), ("split_den", ctypes.c_int),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
 
 
 class TosError(RuntimeError):
@@ -58,6 +59,10 @@ def lib():
         L.tos_attn_fwd.restype = ctypes.c_int
         L.tos_fwd_opts_default.argtypes = [ctypes.POINTER(tos_fwd_opts)]
         L.tos_fwd_opts_default.restype = ctypes.c_int
+        L.tos_attn_fwd_workspace_size.argtypes = [i64, i64, i64, i64, ctypes.c_int, ctypes.c_int,
+                                                  ctypes.POINTER(tos_fwd_opts),
+                                                  ctypes.POINTER(ctypes.c_size_t)]
+        L.tos_attn_fwd_workspace_size.restype = ctypes.c_int
         L.tos_attn_fwd_flops.argtypes = [i64, i64, i64, i64, ctypes.c_int]
         L.tos_attn_fwd_flops.restype = ctypes.c_double
         L.tos_status_string.argtypes = [ctypes.c_int]
@@ -98,6 +103,33 @@ def tos_attn_fwd(q, k, v, o, lse, B, H, N, d, causal, scale, dtype, opts=None, s
     return lib().tos_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H),
                               int(N), int(d), int(causal), float(scale), int(dtype),
                               ctypes.byref(opts) if opts is not None else None, _stream(stream))
+
+
+def tos_attn_fwd_workspace_size(B, H, N, d, causal, dtype, opts=None):
+    """Bytes of device workspace tos_attn_fwd would use (0: none); raises TosError."""
+    n = ctypes.c_size_t(0)
+    rc = lib().tos_attn_fwd_workspace_size(int(B), int(H), int(N), int(d), int(causal), int(dtype),
+                                           ctypes.byref(opts) if opts is not None else None,
+                                           ctypes.byref(n))
+    if rc != TOS_OK:
+        raise TosError(rc)
+    return int(n.value)
+
+
+_workspaces = {}
+
+
+def workspace(nbytes, device):
+    """A cached device buffer of at least nbytes on `device` (torch allocates it;
+    the library allocates nothing).  Calls on one device share it, in stream
+    order on the stream they are launched on."""
+    import torch
+    key = str(device)
+    buf = _workspaces.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+        _workspaces[key] = buf
+    return buf
 
 
 def tos_attn_fwd_flops(B, H, N, d, causal):
@@ -208,8 +240,14 @@ def check_tensors(q, k, v, dtype=None, out=None, lse=None, fallback_tiles=None):
 
 def attn_fwd(q, k, v, causal=False, scale=None, dtype=None, x_tile=32, split="valu",
              fallback="off", tau=0.0, descale=None, with_lse=True, fallback_tiles=None,
-             out=None, lse=None, stream=None, schedule="cosched", share=None):
+             out=None, lse=None, stream=None, schedule="cosched", share=None,
+             use_workspace=True):
     """Allocate O (and lse) with torch and run tos_attn_fwd on the current stream.
+
+    With use_workspace (the default) a problem with fewer query blocks than
+    compute units gets the device workspace tos_attn_fwd_workspace_size asks
+    for (a cached torch buffer), so that its query blocks' keys are cut into
+    pieces across the compute units; use_workspace=False runs whole blocks.
 
     q, k, v: contiguous CUDA tensors [B, H, N, d] of float32, bfloat16, float16
     or float8_e4m3fn (then `descale` = {"q":..., "k":..., "v":...} is required).
@@ -227,6 +265,11 @@ def attn_fwd(q, k, v, causal=False, scale=None, dtype=None, x_tile=32, split="va
     if not with_lse:
         lse = None
     op = make_opts(x_tile, split, fallback, tau, descale, fallback_tiles, schedule, share)
+    if use_workspace:
+        nbytes = tos_attn_fwd_workspace_size(B, H, N, d, causal, _DTYPE_CODES[dtype], op)
+        if nbytes > 0:
+            op.workspace = workspace(nbytes, q.device).data_ptr()
+            op.workspace_bytes = nbytes
     rc = tos_attn_fwd(q, k, v, o, lse, B, H, N, d, causal, scale, _DTYPE_CODES[dtype], op,
                       stream)
     if rc != TOS_OK:

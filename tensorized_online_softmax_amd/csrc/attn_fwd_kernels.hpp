@@ -25,6 +25,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "pieces.hpp"
 #include "softmax_tile.hpp"
 
 namespace tos {
@@ -87,6 +88,12 @@ struct FwdArgs {
   float tau;         // fallback threshold, log2 units
   int* fallback_tiles;   // per-row tile counter, or nullptr
   int count_x;       // > 0: count the X-row tiles of this size as per-row (FORCE)
+  // 16-bit kernels: items cut into pieces of at most split_c key blocks
+  // (pieces.hpp; 0 = whole items), nunits work units in all, and the
+  // workspace of the pieces' partial results (piece_floats(d) per unit)
+  int split_c;
+  int nunits;
+  float* ws;
 };
 
 constexpr int kWaves = 4;
@@ -348,58 +355,67 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_h16(FwdArgs a) {
   // derived from it (block ranges, LDS slots, descriptors) stays scalar
   const int tid = threadIdx.x, lane = tid & 63, ln = lane & 31, hf = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // Persistent workgroups: workgroup g of G runs items (query blocks of a
-  // head) item_of(0, g), item_of(1, g), ... until they run out.
+  // Persistent workgroups: workgroup g of G runs units item_of(0, g),
+  // item_of(1, g), ... until they run out.  A unit is an item (a query block of
+  // a head) or, with a.split_c > 0, a piece of one: a range of its key blocks
+  // (pieces.hpp), whose partial O and lse go to the workspace.
   const int N = a.N;
   const int nblk = (N + kBc - 1) / kBc;
-  const int nitems = a.BH * a.nqb;
+  const int nunits = a.nunits;
   const int nwg = gridDim.x, gid = blockIdx.x;
-  // key blocks of an item: all of them, or (causal) up to its last query
-  auto item_jend = [&](int q0_) { return CAUSAL ? (min(q0_ + kPBr, N) - 1) / kBc + 1 : nblk; };
 
-  // the current item (wave-uniform, but qrow, qvalid and klim)
-  int bh = 0, q0 = 0, qrow = 0, jend = 0, jend_w = 0, klim = 0;
-  bool qvalid = false;
+  // the current unit (wave-uniform, but qrow, qvalid and klim); key blocks are
+  // counted from the unit's first one, jb0
+  int bh = 0, q0 = 0, qrow = 0, jend = 0, jend_w = 0, klim = 0, jb0 = 0, unit = 0;
+  bool qvalid = false, part = false;
   size_t head = 0;
   u32x4 kdesc = {}, vdesc = {};
+  // K (V) of head bh from key block jb on: rows past N read as zeros
+  auto kv_desc = [&](const void* base, size_t head_, int jb) {
+    return buffer_desc((const E*)base + head_ + (size_t)jb * kBc * D, (unsigned)(N - jb * kBc) * RB);
+  };
   auto set_item = [&](int it) {
-    int qb;
-    item_coords(a, CAUSAL, it, bh, qb);
-    q0 = qb * kPBr;
+    const Piece pc = piece_of(it, a.BH, a.nqb, N, CAUSAL, a.split_c);
+    bh = pc.bh;
+    q0 = pc.qb * kPBr;
+    jb0 = pc.jb;
+    unit = it;
+    part = pc.np > 1;
     qrow = q0 + 32 * w + ln;
     qvalid = qrow < N;
     head = (size_t)bh * N * D;
-    kdesc = buffer_desc((const E*)a.k + head, (unsigned)N * RB);
-    vdesc = buffer_desc((const E*)a.v + head, (unsigned)N * RB);
-    jend = item_jend(q0);
+    kdesc = kv_desc(a.k, head, jb0);
+    vdesc = kv_desc(a.v, head, jb0);
+    jend = pc.je - pc.jb;
     // first query of the wave (X = 64: of its pair of waves, which must step
-    // through the same key blocks to exchange their tile maxima)
+    // through the same key blocks to exchange their tile maxima), and the
+    // wave's key blocks within the unit's
     const int wq0 = X == 64 ? q0 + 64 * (w / 2) : q0 + 32 * w;
     const int wrows = X == 64 ? 64 : 32;
-    jend_w = (wq0 >= N) ? 0 : (CAUSAL ? min(wq0 + wrows - 1, N - 1) / kBc + 1 : nblk);
+    const int wend = (wq0 >= N) ? 0 : (CAUSAL ? min(wq0 + wrows - 1, N - 1) / kBc + 1 : nblk);
+    jend_w = max(0, min(wend, pc.je) - pc.jb);
     klim = qvalid ? (CAUSAL ? qrow + 1 : N) : 0;       // keys this lane may see
   };
-  // The next item's first K and V blocks are loaded by this item's last steps
-  // (the ring continues across items) when this item's block count is a
+  // The next unit's first K and V blocks are loaded by this unit's last steps
+  // (the ring continues across units) when this unit's block count is a
   // multiple of the ring size, so that those blocks land in the slots the
-  // next item expects them in.
-  // Its Q fragments are loaded in this item's last step, after the last use
-  // of this item's.
+  // next unit expects them in.
+  // Its Q fragments are loaded in this unit's last step, after the last use
+  // of this unit's.
   bool pref_next = false;
   int jend_n = 0, qrow_n = 0;
   bool qvalid_n = false;
   size_t head_n = 0;
   u32x4 kdesc_n = {}, vdesc_n = {};
   auto set_next = [&](int it) {
-    pref_next = it < nitems && jend % kRing == 0;
+    pref_next = it < nunits && jend % kRing == 0;
     if (pref_next) {
-      int bh_n, qb_n;
-      item_coords(a, CAUSAL, it, bh_n, qb_n);
-      head_n = (size_t)bh_n * N * D;
-      kdesc_n = buffer_desc((const E*)a.k + head_n, (unsigned)N * RB);
-      vdesc_n = buffer_desc((const E*)a.v + head_n, (unsigned)N * RB);
-      jend_n = item_jend(qb_n * kPBr);
-      qrow_n = qb_n * kPBr + 32 * w + ln;
+      const Piece pc = piece_of(it, a.BH, a.nqb, N, CAUSAL, a.split_c);
+      head_n = (size_t)pc.bh * N * D;
+      kdesc_n = kv_desc(a.k, head_n, pc.jb);
+      vdesc_n = kv_desc(a.v, head_n, pc.jb);
+      jend_n = pc.je - pc.jb;
+      qrow_n = pc.qb * kPBr + 32 * w + ln;
       qvalid_n = qrow_n < N;
     }
   };
@@ -524,7 +540,7 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_h16(FwdArgs a) {
   // Key of register r of tile t in block j: j*Bc + 32t + 8(r/4) + 4hf + r%4.
   // Only a wave's last block can hold keys past the diagonal or past N.
   auto mask_block = [&](int j, f32x16& s0, f32x16& s1) {
-    const int kb = j * kBc;
+    const int kb = (jb0 + j) * kBc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int key = kb + 8 * (r / 4) + 4 * hf + (r % 4);
@@ -899,6 +915,28 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_h16(FwdArgs a) {
     if constexpr (!ROWSUM_ALL) l += pair_reduce(lsum, [](float x, float y) { return x + y; });
     const float le = pair_reduce(lexact, [](float x, float y) { return x + y; });
     const float inv = l > 0.0f ? a.o_scale / l : 0.0f;
+    const float lse_v = le > 0.0f ? a.lse_scale * st.ref + (__logf(le) - (float)Elem16<E>::kPreLog2 * 0.69314718f)
+                                  : -__builtin_inff();
+    if (part) {
+      // a piece of an item: its O (normalised by its own row sums, fp32) and
+      // lse go to the unit's workspace slot, for the merge kernel
+      float* slot = a.ws + (size_t)unit * piece_floats(D);
+      const int r = 32 * w + ln;
+      if (qvalid) {
+#pragma unroll
+        for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const float4 ov = make_float4(oacc[mt][4 * g] * inv, oacc[mt][4 * g + 1] * inv,
+                                          oacc[mt][4 * g + 2] * inv, oacc[mt][4 * g + 3] * inv);
+            *(float4*)(slot + (size_t)r * D + 32 * mt + 8 * g + 4 * hf) = ov;
+          }
+        if (hf == 0) slot[kPieceRows * D + r] = lse_v;
+      }
+      o_nrows = 0;          // nothing for flush()
+      lse_rows = nullptr;
+      return;
+    }
     // (the lane's row, opaque here: its addresses are formed here, not
     // hoisted out of the item loop to hold registers through it)
     int sr = ln;
@@ -922,8 +960,7 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_h16(FwdArgs a) {
     o_rows = (E*)a.o + head + (size_t)wq0 * D;
     lse_rows = a.lse == nullptr ? nullptr : a.lse + (size_t)bh * N + wq0;
     o_nrows = max(0, min(32, N - wq0));
-    lse_out = le > 0.0f ? a.lse_scale * st.ref + (__logf(le) - (float)Elem16<E>::kPreLog2 * 0.69314718f)
-                        : -__builtin_inff();
+    lse_out = lse_v;
     count_tiles<X, FB_AUTO>(a, st, lane, qrow);
   };
   auto flush = [&]() {
@@ -1012,7 +1049,7 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_h16(FwdArgs a) {
     if (!pref_next) asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
 
     finish();
-    if (it_next >= nitems) {
+    if (it_next >= nunits) {
       flush();
       break;
     }
@@ -1020,6 +1057,67 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_h16(FwdArgs a) {
     it = it_next;
     set_item(it);
   }
+}
+
+// ---------------------------------------------------------------------------
+// Merge of the pieces of each item (pieces.hpp); items of one piece wrote their
+// rows directly.  For each row, with the pieces' partial (O_c, lse_c):
+//   lse = m + ln sum_c exp(lse_c - m), m = max_c lse_c;  O = sum_c exp(lse_c - lse) O_c.
+// A piece that held no key of the row has lse_c = -inf and weight 0 (every row
+// has key 0, in the item's first piece).  Workgroup (item, p) covers rows
+// [p * RPW, (p + 1) * RPW) of the item, one thread per 8 consecutive columns of
+// a row, so that every load of the merge is in flight at once.
+// ---------------------------------------------------------------------------
+template <int D> constexpr int kMergeRowsPerWg = 256 / (D / 8);
+
+template <typename E, int D, bool CAUSAL>
+__global__ __launch_bounds__(256) void attn_merge_h16(FwdArgs a) {
+  constexpr int TPR = D / 8;                   // threads per row
+  constexpr int RPW = kMergeRowsPerWg<D>;      // rows per workgroup
+  constexpr int NWI = kPieceRows / RPW;        // workgroups per item
+  const int it = blockIdx.x / NWI;             // item: (head, query block), heaviest first
+  const int BH = a.BH, N = a.N;
+  const int bh = it % BH, L = it / BH, qb = CAUSAL ? a.nqb - 1 - L : L;
+  // the item's first unit: the units of the heavier levels, then this level's
+  // heads before bh
+  int first = 0, np = 1;
+  for (int l = 0; l <= L; ++l) {
+    const int q = CAUSAL ? a.nqb - 1 - l : l;
+    const int p = pieces_of(qblock_blocks(q, N, CAUSAL), a.split_c);
+    if (l < L) first += BH * p;
+    else { first += bh * p; np = p; }
+  }
+  if (np <= 1) return;
+  const int t = threadIdx.x, col = 8 * (t % TPR);
+  const int r = (blockIdx.x % NWI) * RPW + t / TPR;
+  const int row = qb * kPieceRows + r;
+  if (row >= N) return;
+  const float* base = a.ws + (size_t)first * piece_floats(D);
+  const size_t stride = (size_t)piece_floats(D);
+  float m = -__builtin_inff();
+  for (int c = 0; c < np; ++c) m = fmaxf(m, base[c * stride + kPieceRows * D + r]);
+  float acc[8] = {};
+  float sum = 0.0f;
+  if (m != -__builtin_inff()) {
+#pragma unroll 4
+    for (int c = 0; c < np; ++c) {
+      const float* slot = base + c * stride;
+      const float lc = slot[kPieceRows * D + r];
+      const float wgt = lc == -__builtin_inff() ? 0.0f : __expf(lc - m);
+      const float4 x0 = *(const float4*)(slot + (size_t)r * D + col);
+      const float4 x1 = *(const float4*)(slot + (size_t)r * D + col + 4);
+      sum += wgt;
+      acc[0] += wgt * x0.x; acc[1] += wgt * x0.y; acc[2] += wgt * x0.z; acc[3] += wgt * x0.w;
+      acc[4] += wgt * x1.x; acc[5] += wgt * x1.y; acc[6] += wgt * x1.z; acc[7] += wgt * x1.w;
+    }
+  }
+  const float inv = sum > 0.0f ? 1.0f / sum : 0.0f;
+  typedef E ev8_t __attribute__((ext_vector_type(8)));
+  ev8_t ov;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) ov[u] = (E)(acc[u] * inv);
+  *(ev8_t*)((E*)a.o + (size_t)bh * N * D + (size_t)row * D + col) = ov;
+  if (a.lse != nullptr && col == 0) a.lse[(size_t)bh * N + row] = sum > 0.0f ? m + __logf(sum) : m;
 }
 
 // ---------------------------------------------------------------------------

@@ -26,12 +26,18 @@ template <typename E, int D, bool CAUSAL, int X, int PLAN, bool FB, bool SEQ = f
 static hipError_t go_h16(const FwdArgs& a, hipStream_t s) {
   FwdArgs arg = a;
   arg.nqb = (a.N + kPBr - 1) / kPBr;
-  const dim3 grid((unsigned)persistent_grid(arg.BH * arg.nqb)), block(kPThreads);
+  arg.nunits = (int)units_of(arg.BH, arg.nqb, arg.N, CAUSAL, arg.split_c);
+  const dim3 grid((unsigned)persistent_grid(arg.nunits)), block(kPThreads);
   // hipLaunchKernel reports this launch's own status (hipGetLastError could
   // return an error left behind by an earlier, unrelated call)
   void* params[] = {&arg};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&attn_fwd_h16<E, D, CAUSAL, X, PLAN, FB, SEQ>), grid,
-                         block, params, 0, s);
+  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&attn_fwd_h16<E, D, CAUSAL, X, PLAN, FB, SEQ>),
+                                 grid, block, params, 0, s);
+  if (e != hipSuccess || arg.split_c <= 0) return e;
+  // the pieces' partial results, merged per item on the same stream
+  const unsigned wgs = (unsigned)(arg.BH * arg.nqb) * (unsigned)(kPieceRows / kMergeRowsPerWg<D>);
+  return hipLaunchKernel(reinterpret_cast<const void*>(&attn_merge_h16<E, D, CAUSAL>), dim3(wgs), dim3(256),
+                         params, 0, s);
 }
 
 template <typename E, int D, bool CAUSAL>

@@ -68,11 +68,16 @@ tos_status tos_fwd_opts_default(tos_fwd_opts* opts) {
   return TOS_OK;
 }
 
-tos_status tos_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-                        int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
-                        tos_dtype dtype, const tos_fwd_opts* opts, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Everything about a call but its pointers: options, sizes and the kernel
+// choice.  Returns TOS_OK with *empty set when there is nothing to compute.
+tos_status prepare(const tos_fwd_opts* opts, int64_t B, int64_t H, int64_t N, int64_t d, int causal,
+                   tos_dtype dtype, tos_fwd_opts& op, tos::KernelChoice& kc, bool* empty) {
+  *empty = false;
   // ---- options
-  tos_fwd_opts op;
   tos_fwd_opts_default(&op);
   if (opts != nullptr) {
     if (opts->size != (int)sizeof(tos_fwd_opts)) return TOS_ERR_INVALID_ARG;
@@ -94,18 +99,21 @@ tos_status tos_attn_fwd(const void* q, const void* k, const void* v, void* o, fl
     return TOS_ERR_INVALID_ARG;
   if (op.schedule != TOS_SCHEDULE_COSCHED && op.schedule != TOS_SCHEDULE_SEQUENTIAL)
     return TOS_ERR_INVALID_ARG;
+  if (op.workspace == nullptr && op.workspace_bytes != 0) return TOS_ERR_INVALID_ARG;
 
-  // ---- sizes and scalars
+  // ---- sizes
   if (dtype != TOS_F32 && dtype != TOS_BF16 && dtype != TOS_FP8_E4M3 && dtype != TOS_F16)
     return TOS_ERR_INVALID_ARG;
   if (B < 0 || H < 0 || N < 0 || d < 0) return TOS_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return TOS_ERR_INVALID_ARG;
-  if (!std::isfinite(scale) || !(scale > 0.0f)) return TOS_ERR_INVALID_ARG;
   if (dtype == TOS_FP8_E4M3) {
     for (float s : {op.q_descale, op.k_descale, op.v_descale})
       if (!std::isfinite(s) || !(s > 0.0f)) return TOS_ERR_INVALID_ARG;
   }
-  if (B == 0 || H == 0 || N == 0) return TOS_OK;   // nothing to compute
+  if (B == 0 || H == 0 || N == 0) {   // nothing to compute
+    *empty = true;
+    return TOS_OK;
+  }
   if (d != 64 && d != 128) return TOS_ERR_UNSUPPORTED;
   const int64_t BH = B * H;
   const int64_t nqb = (N + tos::kBr - 1) / tos::kBr;
@@ -114,22 +122,7 @@ tos_status tos_attn_fwd(const void* q, const void* k, const void* v, void* o, fl
       BH * nqb > INT32_MAX || N * d * (int64_t)in_elem_bytes(dtype) > INT32_MAX)
     return TOS_ERR_UNSUPPORTED;
 
-  // ---- pointers: required, aligned, output not overlapping anything
-  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr) return TOS_ERR_INVALID_ARG;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
-      !aligned(lse, 4))
-    return TOS_ERR_INVALID_ARG;
-  const size_t n_elem = (size_t)BH * (size_t)N * (size_t)d;
-  const size_t in_b = n_elem * in_elem_bytes(dtype), out_b = n_elem * out_elem_bytes(dtype);
-  const size_t lse_b = lse ? (size_t)BH * (size_t)N * sizeof(float) : 0;
-  for (const void* in : {q, k, v}) {
-    if (overlaps(o, out_b, in, in_b)) return TOS_ERR_INVALID_ARG;
-    if (overlaps(lse, lse_b, in, in_b)) return TOS_ERR_INVALID_ARG;
-  }
-  if (overlaps(o, out_b, lse, lse_b)) return TOS_ERR_INVALID_ARG;
-
   // ---- kernel choice
-  tos::KernelChoice kc;
   kc.d = (int)d;
   kc.causal = causal != 0;
   kc.x = op.fallback == TOS_FALLBACK_FORCE ? 1 : op.x_tile;
@@ -181,6 +174,71 @@ tos_status tos_attn_fwd(const void* q, const void* k, const void* v, void* o, fl
   // X = 64 (tiles of two waves): the 16-bit kernels with the vector row sum
   if (kc.x == 64 && (!h16 || kc.plan != tos::kPlanValu)) return TOS_ERR_UNSUPPORTED;
 
+  return TOS_OK;
+}
+
+// Pieces for a 16-bit call (pieces.hpp): the piece length in key blocks (0:
+// whole query blocks) and the workspace bytes they need.  Only with the
+// fallback off: a piece's switch to per-row maxima would be its own.
+int split_for(const tos_fwd_opts& op, const tos::KernelChoice& kc, tos_dtype dtype, int64_t BH, int64_t N,
+              int64_t d, size_t* bytes) {
+  *bytes = 0;
+  if ((dtype != TOS_BF16 && dtype != TOS_F16) || op.fallback != TOS_FALLBACK_OFF) return 0;
+  const int C = tos::split_blocks((int)BH, (int)N, kc.causal, tos::device_cus());
+  if (C <= 0) return 0;
+  const int nqb = (int)((N + tos::kPieceRows - 1) / tos::kPieceRows);
+  const long long units = tos::units_of((int)BH, nqb, (int)N, kc.causal, C);
+  *bytes = (size_t)units * (size_t)tos::piece_floats((int)d) * sizeof(float);
+  return C;
+}
+
+}  // namespace
+
+extern "C" {
+
+tos_status tos_attn_fwd_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d, int causal,
+                                       tos_dtype dtype, const tos_fwd_opts* opts, size_t* bytes) {
+  if (bytes == nullptr) return TOS_ERR_INVALID_ARG;
+  *bytes = 0;
+  tos_fwd_opts op;
+  tos::KernelChoice kc;
+  bool empty = false;
+  const tos_status st = prepare(opts, B, H, N, d, causal, dtype, op, kc, &empty);
+  if (st != TOS_OK || empty) return st;
+  split_for(op, kc, dtype, B * H, N, d, bytes);
+  return TOS_OK;
+}
+
+tos_status tos_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
+                        tos_dtype dtype, const tos_fwd_opts* opts, void* stream) {
+  tos_fwd_opts op;
+  tos::KernelChoice kc;
+  bool empty = false;
+  if (!std::isfinite(scale) || !(scale > 0.0f)) return TOS_ERR_INVALID_ARG;
+  const tos_status st = prepare(opts, B, H, N, d, causal, dtype, op, kc, &empty);
+  if (st != TOS_OK || empty) return st;
+  const int64_t BH = B * H;
+  const int64_t nqb = (N + tos::kBr - 1) / tos::kBr;
+
+  // ---- pointers: required, aligned, outputs and workspace overlapping nothing
+  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr) return TOS_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(lse, 4) || !aligned(op.workspace, 16))
+    return TOS_ERR_INVALID_ARG;
+  const size_t n_elem = (size_t)BH * (size_t)N * (size_t)d;
+  const size_t in_b = n_elem * in_elem_bytes(dtype), out_b = n_elem * out_elem_bytes(dtype);
+  const size_t lse_b = lse ? (size_t)BH * (size_t)N * sizeof(float) : 0;
+  const size_t ws_b = op.workspace_bytes;
+  for (const void* in : {q, k, v}) {
+    if (overlaps(o, out_b, in, in_b)) return TOS_ERR_INVALID_ARG;
+    if (overlaps(lse, lse_b, in, in_b)) return TOS_ERR_INVALID_ARG;
+    if (overlaps(op.workspace, ws_b, in, in_b)) return TOS_ERR_INVALID_ARG;
+  }
+  if (overlaps(o, out_b, lse, lse_b)) return TOS_ERR_INVALID_ARG;
+  if (overlaps(op.workspace, ws_b, o, out_b) || overlaps(op.workspace, ws_b, lse, lse_b))
+    return TOS_ERR_INVALID_ARG;
+
   tos::FwdArgs a;
   a.q = q;
   a.k = k;
@@ -206,6 +264,17 @@ tos_status tos_attn_fwd(const void* q, const void* k, const void* v, void* o, fl
   a.count_x = op.fallback == TOS_FALLBACK_FORCE ? op.x_tile : 0;
   if (op.fallback == TOS_FALLBACK_AUTO && op.x_tile == 1) a.count_x = 0;
 
+  // pieces of query blocks, when the workspace holds them
+  a.split_c = 0;
+  a.ws = nullptr;
+  size_t need = 0;
+  const int C = split_for(op, kc, dtype, BH, N, d, &need);
+  if (C > 0 && op.workspace != nullptr && op.workspace_bytes >= need) {
+    a.split_c = C;
+    a.ws = (float*)op.workspace;
+  }
+  a.nunits = (int)(BH * nqb);
+
   const hipStream_t s = (hipStream_t)stream;
   hipError_t e = hipErrorNotSupported;
   if (dtype == TOS_BF16)
@@ -218,9 +287,9 @@ tos_status tos_attn_fwd(const void* q, const void* k, const void* v, void* o, fl
     e = tos::launch_fp8(a, kc, s);
   if (log_enabled())
     std::fprintf(stderr, "[tos] dtype=%d B=%lld H=%lld N=%lld d=%d causal=%d X=%d plan=0x%x "
-                 "fallback=%d sequential=%d items=%lld: %s\n", (int)dtype, (long long)B, (long long)H,
+                 "fallback=%d sequential=%d items=%lld pieces=%d: %s\n", (int)dtype, (long long)B, (long long)H,
                  (long long)N, kc.d, (int)kc.causal, kc.x, kc.plan, op.fallback,
-                 (int)kc.seq, (long long)(BH * nqb), hipGetErrorString(e));
+                 (int)kc.seq, (long long)(BH * nqb), a.split_c, hipGetErrorString(e));
   if (e == hipErrorNotSupported) return TOS_ERR_UNSUPPORTED;
   return e == hipSuccess ? TOS_OK : TOS_ERR_HIP;
 }

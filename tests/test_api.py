@@ -136,6 +136,11 @@ def opts(**kw):
      tb.TOS_ERR_UNSUPPORTED),
     (dict(B=70000, H=70000), tb.TOS_ERR_UNSUPPORTED),       # grid beyond 2^31
     # empty problems: nothing to do, and no pointer is needed
+    # a workspace size with no workspace, a misaligned or overlapping workspace
+    (dict(opts=opts(workspace_bytes=64)), tb.TOS_ERR_INVALID_ARG),
+    (dict(opts=opts(workspace=0x600008, workspace_bytes=64)), tb.TOS_ERR_INVALID_ARG),
+    (dict(opts=opts(workspace=Q + 64, workspace_bytes=64)), tb.TOS_ERR_INVALID_ARG),
+    (dict(opts=opts(workspace=O, workspace_bytes=64)), tb.TOS_ERR_INVALID_ARG),
     (dict(B=0, q=None, k=None, v=None, o=None), tb.TOS_OK),
     (dict(H=0), tb.TOS_OK),
     (dict(N=0), tb.TOS_OK),
@@ -186,3 +191,25 @@ def test_binding_rejects_bad_tensors():
         tb.attn_fwd(q, _t(), _t(), dtype="f16")
     with pytest.raises(ValueError, match="CUDA"):
         tb.attn_fwd(q, _t(), _t())
+
+
+def test_workspace_size():
+    """Pieces only where query blocks are fewer than compute units (256 when no
+    device is visible), 16-bit inputs and the fallback off; at most
+    256 x 256 x (d + 1) floats."""
+    ws = tb.tos_attn_fwd_workspace_size
+    cap = 256 * 256 * 129 * 4
+    assert ws(2, 4, 4096, 128, 1, tb.TOS_BF16) == cap      # one GPU's share of 8: 128 blocks
+    assert ws(2, 32, 4096, 128, 1, tb.TOS_BF16) == 0       # 1024 query blocks
+    assert ws(4, 16, 1024, 64, 0, tb.TOS_BF16) == 0        # 256 query blocks
+    assert 0 < ws(1, 4, 1000, 64, 1, tb.TOS_F16) <= 256 * 256 * 65 * 4
+    assert ws(1, 1, 128, 64, 0, tb.TOS_BF16) == 0          # 2 key blocks: nothing to cut
+    assert ws(1, 2, 4096, 128, 0, tb.TOS_F32) == 0
+    assert ws(1, 2, 4096, 128, 0, tb.TOS_FP8_E4M3, opts(q_descale=1.0)) == 0
+    assert ws(1, 2, 4096, 128, 0, tb.TOS_BF16, opts(fallback=1)) == 0
+    assert ws(0, 2, 4096, 128, 0, tb.TOS_BF16) == 0
+    with pytest.raises(tb.TosError):
+        ws(1, 2, 4096, 96, 0, tb.TOS_BF16)
+    with pytest.raises(tb.TosError):
+        ws(1, 2, 4096, 128, 0, tb.TOS_BF16, opts(x_tile=8))
+    assert tb.lib().tos_attn_fwd_workspace_size(1, 1, 64, 64, 0, 1, None, None) == tb.TOS_ERR_INVALID_ARG

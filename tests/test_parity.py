@@ -112,6 +112,43 @@ def test_split_plans(dtype, d, causal, N, split, share):
                  f"{split} {share} {dtype} d={d} causal={causal} N={N}")
 
 
+# Problems with fewer 256-row query blocks than compute units: the binding
+# passes a workspace, and each query block's keys are cut into pieces on
+# separate compute units, merged by a second kernel (ragged N, both head dims,
+# causal and not, several tile heights, without lse too).
+@pytest.mark.parametrize("dtype,B,H,N,d,causal,x_tile", [
+    ("bf16", 1, 1, 4096, 128, True, 32),
+    ("bf16", 1, 2, 4096, 128, False, 32),
+    ("bf16", 1, 4, 1000, 64, True, 32),
+    ("bf16", 2, 3, 3000, 128, False, 16),
+    ("bf16", 1, 3, 2900, 64, True, 1),
+    ("bf16", 2, 2, 2500, 128, True, 64),
+    ("f16", 1, 2, 4096, 128, True, 32),
+    ("f16", 2, 1, 3333, 64, False, 32),
+])
+@pytest.mark.parametrize("with_lse", [True, False])
+def test_key_pieces(dtype, B, H, N, d, causal, x_tile, with_lse):
+    nbytes = tb.tos_attn_fwd_workspace_size(B, H, N, d, causal, tb._DTYPE_CODES[dtype],
+                                            tb.make_opts(x_tile=x_tile))
+    assert nbytes > 0
+    inp = _inp(B, H, N, d, dtype, seed=500 + N + d + H)
+    dev = to_device(inp)
+    o, lse = tb.attn_fwd(dev["q"], dev["k"], dev["v"], causal=causal, scale=inp["scale"],
+                         x_tile=x_tile, with_lse=with_lse)
+    o_w, lse_w = tb.attn_fwd(dev["q"], dev["k"], dev["v"], causal=causal, scale=inp["scale"],
+                             x_tile=x_tile, use_workspace=False)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle_exact(inp, causal)
+    o64 = o.to(torch.float64).cpu().numpy().reshape(o_ref.shape)
+    l64 = (lse if with_lse else lse_w).to(torch.float64).cpu().numpy().reshape(lse_ref.shape)
+    assert_close(o64, o_ref, l64, lse_ref, dtype,
+                 f"pieces {dtype} B={B} H={H} N={N} d={d} causal={causal} X={x_tile}")
+    # the whole-block run agrees to within the same bounds
+    assert_close(o_w.to(torch.float64).cpu().numpy().reshape(o_ref.shape), o_ref,
+                 lse_w.to(torch.float64).cpu().numpy().reshape(lse_ref.shape), lse_ref, dtype,
+                 f"whole blocks {dtype} B={B} H={H} N={N} d={d}")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32", "fp8"])
 def test_without_lse(dtype):
     """lse = NULL: O is the same as with lse, and matches the oracle."""
