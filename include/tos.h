@@ -58,7 +58,9 @@ typedef enum {
     TOS_ERR_UNSUPPORTED = 2,   /* valid request outside what the kernels cover
                                   (head dim not 64/128, size limits, option not
                                   available for the dtype)                        */
-    TOS_ERR_HIP = 3            /* the HIP runtime rejected the launch             */
+    TOS_ERR_HIP = 3,           /* the HIP runtime rejected the launch             */
+    TOS_ERR_SCRATCH = 4        /* tos_attn_fwd_noalloc: the problem needs more
+                                  workspace than the library's static area holds */
 } tos_status;
 
 typedef enum {
@@ -193,6 +195,23 @@ typedef struct {
 tos_status tos_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                         int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
                         tos_dtype dtype, const tos_fwd_opts* opts, void* stream);
+
+/*
+ * tos_attn_fwd_noalloc -- tos_attn_fwd for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments and results; opts->workspace must be NULL
+ * (TOS_ERR_INVALID_ARG otherwise): the pieces' workspace is a static device
+ * array of 33.8 MB (256 x 256 x 129 floats, what any call with d <= 128 can
+ * need), which each GPU the library runs on holds until the process ends.  A
+ * call that would need more returns TOS_ERR_SCRATCH.  The call allocates
+ * nothing; its first call on a device looks the array's address up.  Every
+ * call on one GPU shares that array: calls that overlap in time on one GPU
+ * (other streams, other host threads) race on it and must be serialised by
+ * the caller; its contents on entry do not matter.
+ */
+tos_status tos_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                                int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
+                                tos_dtype dtype, const tos_fwd_opts* opts, void* stream);
 
 /* Device workspace, in bytes, that tos_attn_fwd with these arguments and
  * options (NULL = defaults) would use to cut query blocks into pieces on the

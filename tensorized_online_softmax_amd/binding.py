@@ -11,14 +11,14 @@ import os
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libtos.so")
 
-TOS_OK, TOS_ERR_INVALID_ARG, TOS_ERR_UNSUPPORTED, TOS_ERR_HIP = 0, 1, 2, 3
+TOS_OK, TOS_ERR_INVALID_ARG, TOS_ERR_UNSUPPORTED, TOS_ERR_HIP, TOS_ERR_SCRATCH = 0, 1, 2, 3, 4
 TOS_F32, TOS_BF16, TOS_FP8_E4M3, TOS_F16 = 0, 1, 2, 3
 (TOS_SPLIT_VALU, TOS_SPLIT_ROWSUM_MFMA, TOS_SPLIT_SCALE_MFMA, TOS_SPLIT_HSPLIT, TOS_SPLIT_VSPLIT,
  TOS_SPLIT_ALL_MFMA) = range(6)
 TOS_FALLBACK_OFF, TOS_FALLBACK_AUTO, TOS_FALLBACK_FORCE = 0, 1, 2
 TOS_SCHEDULE_COSCHED, TOS_SCHEDULE_SEQUENTIAL = 0, 1
 
-EXPORTED = ("tos_attn_fwd", "tos_fwd_opts_default", "tos_attn_fwd_flops",
+EXPORTED = ("tos_attn_fwd", "tos_attn_fwd_noalloc", "tos_fwd_opts_default", "tos_attn_fwd_flops",
             "tos_attn_fwd_workspace_size", "tos_status_string", "tos_version")
 
 
@@ -57,6 +57,8 @@ def lib():
         L.tos_attn_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int,
                                    ctypes.c_float, ctypes.c_int, ctypes.POINTER(tos_fwd_opts), vp]
         L.tos_attn_fwd.restype = ctypes.c_int
+        L.tos_attn_fwd_noalloc.argtypes = L.tos_attn_fwd.argtypes
+        L.tos_attn_fwd_noalloc.restype = ctypes.c_int
         L.tos_fwd_opts_default.argtypes = [ctypes.POINTER(tos_fwd_opts)]
         L.tos_fwd_opts_default.restype = ctypes.c_int
         L.tos_attn_fwd_workspace_size.argtypes = [i64, i64, i64, i64, ctypes.c_int, ctypes.c_int,
@@ -103,6 +105,15 @@ def tos_attn_fwd(q, k, v, o, lse, B, H, N, d, causal, scale, dtype, opts=None, s
     return lib().tos_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H),
                               int(N), int(d), int(causal), float(scale), int(dtype),
                               ctypes.byref(opts) if opts is not None else None, _stream(stream))
+
+
+def tos_attn_fwd_noalloc(q, k, v, o, lse, B, H, N, d, causal, scale, dtype, opts=None,
+                         stream=None):
+    """Direct call of the allocation-free entry point; returns the tos_status code."""
+    return lib().tos_attn_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B),
+                                      int(H), int(N), int(d), int(causal), float(scale),
+                                      int(dtype), ctypes.byref(opts) if opts is not None else None,
+                                      _stream(stream))
 
 
 def tos_attn_fwd_workspace_size(B, H, N, d, causal, dtype, opts=None):

@@ -45,6 +45,7 @@ const char* tos_status_string(tos_status s) {
     case TOS_ERR_INVALID_ARG: return "TOS_ERR_INVALID_ARG";
     case TOS_ERR_UNSUPPORTED: return "TOS_ERR_UNSUPPORTED";
     case TOS_ERR_HIP: return "TOS_ERR_HIP";
+    case TOS_ERR_SCRATCH: return "TOS_ERR_SCRATCH";
   }
   return "TOS_UNKNOWN_STATUS";
 }

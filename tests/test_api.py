@@ -43,6 +43,7 @@ def test_helpers():
     assert tb.tos_attn_fwd_flops(0, 16, 1024, 64, 0) == 0.0
     assert tb.tos_status_string(tb.TOS_OK) == "TOS_OK"
     assert tb.tos_status_string(tb.TOS_ERR_UNSUPPORTED) == "TOS_ERR_UNSUPPORTED"
+    assert tb.tos_status_string(tb.TOS_ERR_SCRATCH) == "TOS_ERR_SCRATCH"
     assert tb.tos_status_string(99) == "TOS_UNKNOWN_STATUS"
     op = tb.tos_fwd_opts_default()
     assert op.size == ctypes.sizeof(tb.tos_fwd_opts)
