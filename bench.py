@@ -30,16 +30,13 @@ EXP_PER_S = 256 * 4 * 8 * 2.4e9
 HBM_GBPS = 8000.0
 # sources of each dtype's kernel: a committed traffic summary is used only
 # while these are unchanged
+_CSRC = "tensorized_online_softmax_amd/csrc/"
 KERNEL_SOURCES = {
-    "bf16": ["tensorized_online_softmax_amd/csrc/attn_fwd_kernels.hpp",
-             "tensorized_online_softmax_amd/csrc/softmax_tile.hpp"],
-    "f16": ["tensorized_online_softmax_amd/csrc/attn_fwd_kernels.hpp",
-            "tensorized_online_softmax_amd/csrc/softmax_tile.hpp"],
-    "f32": ["tensorized_online_softmax_amd/csrc/attn_fwd_kernels.hpp",
-            "tensorized_online_softmax_amd/csrc/softmax_tile.hpp"],
-    "fp8": ["tensorized_online_softmax_amd/csrc/attn_fwd_kernels.hpp",
-            "tensorized_online_softmax_amd/csrc/attn_fwd_fp8.hpp",
-            "tensorized_online_softmax_amd/csrc/softmax_tile.hpp"],
+    "bf16": [_CSRC + f for f in ("attn_fwd_kernels.hpp", "softmax_tile.hpp", "pieces.hpp")],
+    "f16": [_CSRC + f for f in ("attn_fwd_kernels.hpp", "softmax_tile.hpp", "pieces.hpp")],
+    "f32": [_CSRC + f for f in ("attn_fwd_kernels.hpp", "softmax_tile.hpp", "pieces.hpp")],
+    "fp8": [_CSRC + f for f in ("attn_fwd_kernels.hpp", "attn_fwd_fp8.hpp", "softmax_tile.hpp",
+                                "pieces.hpp")],
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_{workload}.txt")
 
@@ -340,6 +337,87 @@ def time_workload(w, inp, x_tile, split, fallback, schedule, share, steps, warmu
             "ms_per_step": round(ms_per_step, 4), "config": config, "roofline": roofline}
 
 
+# Settings of the vector-interval table (FlashAttention-T, section A4, Fig 9:
+# the share of the iteration in which the matrix unit waits for vector work),
+# each with the matrix-unit cycles of one steady step of a SIMD (two waves of 32
+# query rows x 64 keys): 32 bf16 32x32x16 MFMAs of 32 clocks per wave, 4 more
+# for the matrix-unit row sum, and for everything on the matrix unit also 34
+# fp32 32x32x2 MFMAs of 64 clocks (Z: two tiles of one offset and 16 slices).
+VECTOR_INTERVAL = [
+    ("per_row_sequential", 1, "valu", "sequential", 2 * 32 * 32),   # FA2 analog
+    ("tile32_sequential", 32, "valu", "sequential", 2 * 32 * 32),
+    ("per_row_cosched", 1, "valu", "cosched", 2 * 32 * 32),
+    ("tile16_cosched", 16, "valu", "cosched", 2 * 32 * 32),         # Max16 analog
+    ("tile32_cosched", 32, "valu", "cosched", 2 * 32 * 32),         # FA-T analog
+    ("tile32_rowsum_mfma", 32, "rowsum_mfma", "cosched", 2 * 36 * 32),
+    ("tile32_all_mfma", 32, "all_mfma", "cosched", 2 * (36 * 32 + 34 * 64)),   # AllTensor analog
+]
+
+
+def vector_interval(workload, steps, warmup):
+    """Phase-stamped runs of each setting (s_memtime cycles per wave, summed over
+    the launches): the step cycles of a SIMD against its matrix-unit cycles give
+    the share of the step in which the matrix unit is idle; the sequential
+    schedule's softmax section is its vector-only time.  The stamps wait for
+    themselves, so a traced launch is slower than a plain one (both reported)."""
+    import torch
+    from tensorized_online_softmax_amd import binding, inputs
+    w = inputs.WORKLOADS[workload]
+    if w.dtype != "bf16" or w.d != 128:
+        raise SystemExit("the phase-stamped kernels are the bf16 d=128 ones")
+    torch.cuda.set_device(0)
+    inp = inputs.make_workload(w)
+    q, k, v = (inp[n].cuda() for n in ("q", "k", "v"))
+    o = torch.empty((w.B, w.H, w.N, w.d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
+    trace = torch.zeros(1024 * 1024 // 8, dtype=torch.int64, device="cuda")
+    n = max(3, min(steps, 20))
+    for name, x, split, sched, mfma_clk in VECTOR_INTERVAL:
+        def f(tr=None):
+            binding.attn_fwd(q, k, v, causal=w.causal, scale=w.scale, x_tile=x, split=split,
+                             schedule=sched, out=o, lse=lse, trace=tr)
+        times = {}
+        for kind in ("plain", "traced"):
+            for _ in range(max(2, min(warmup, 5))):
+                f(trace if kind == "traced" else None)
+            trace.zero_()
+            torch.cuda.synchronize()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+            for i in range(n):
+                ev[i].record()
+                f(trace if kind == "traced" else None)
+            ev[n].record()
+            torch.cuda.synchronize()
+            t = sorted(ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(n))
+            times[kind] = t[len(t) // 2]
+        tr = trace.view(-1, 16).cpu().numpy().astype("float64")
+        tr = tr[tr[:, 0] > 0]
+        tot = tr.sum(axis=0)
+        line = {"workload": w.name, "setting": name, "x_tile": x, "softmax_split": split,
+                "schedule": sched, "launches": n,
+                "plain_median_us": round(times["plain"], 2),
+                "traced_median_us": round(times["traced"], 2),
+                "waves": int(tr.shape[0])}
+        if tot[1] > 0:
+            step = tot[2] / tot[1]
+            line.update({"steady_steps": int(tot[1]), "steady_step_clk": round(step, 1),
+                         "phase_a_clk": round(tot[3] / tot[1], 1),
+                         "phase_b_clk": round(tot[4] / tot[1], 1),
+                         "barrier_clk": round(tot[5] / tot[1], 1)})
+        if tot[6] > 0:
+            line.update({"edge_steps": int(tot[6]), "edge_step_clk": round(tot[7] / tot[6], 1),
+                         "edge_softmax_clk": round(tot[8] / tot[6], 1),
+                         "edge_barrier_clk": round(tot[9] / tot[6], 1)})
+        # the matrix unit's idle share of a step of a SIMD (two waves), from the
+        # steady steps when the schedule has them, else from all steps
+        step = line.get("steady_step_clk") or line.get("edge_step_clk")
+        line["mfma_clk_per_simd_step"] = mfma_clk
+        line["vector_interval_ratio"] = round(max(0.0, 1.0 - mfma_clk / step), 4)
+        if sched == "sequential":
+            line["softmax_share_of_step"] = round(tot[8] / tot[7], 4)
+        print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -372,7 +450,14 @@ def main():
                     help="instead of the attention bench: time torch's bf16 GEMM (the vendor "
                          "library) on random and on all-zero data, for the MFMA throughput this "
                          "GPU sustains under its power limit")
+    ap.add_argument("--vector-interval", action="store_true",
+                    help="instead of the attention bench: phase-stamped runs of the ablation's "
+                         "settings (bf16, d=128 workloads) and the matrix unit's idle share of "
+                         "a step; one JSON line per setting")
     args = ap.parse_args()
+    if args.vector_interval:
+        vector_interval(args.workload, args.steps, args.warmup)
+        return
     if args.mfma_ceiling:
         mfma_ceiling()
         return

@@ -169,6 +169,21 @@ typedef struct {
                               and the fallback is off; must not overlap the
                               tensors; its contents on entry do not matter      */
     size_t workspace_bytes;
+    uint64_t* trace;       /* NULL, or a device buffer of trace_bytes: runs a
+                              phase-stamped copy of the kernel (bf16, d = 128,
+                              fallback off; X = 1 / 16 / 32 co-scheduled, X = 1 /
+                              32 sequential, or X = 32 with the matrix-unit row
+                              sum or everything on the matrix unit; else
+                              TOS_ERR_UNSUPPORTED) that adds, per wave, s_memtime
+                              cycles of its steps and their phases to 16 slots at
+                              trace[(workgroup * 8 + wave) * 16]: 0 wave total,
+                              1 steady steps, 2 their cycles, 3 phase A, 4 phase
+                              B, 5 barrier wait, 6 edge steps, 7 their cycles,
+                              8 their softmax section, 9 barrier wait.  The
+                              buffer holds one workgroup per compute unit:
+                              trace_bytes >= compute units * 1024 (else
+                              TOS_ERR_INVALID_ARG); the caller zeroes it     */
+    size_t trace_bytes;
 } tos_fwd_opts;
 
 /*

@@ -29,7 +29,8 @@ class tos_fwd_opts(ctypes.Structure):
                 ("k_descale", ctypes.c_float), ("v_descale", ctypes.c_float),
                 ("fallback_tiles", ctypes.c_void_p), ("schedule", ctypes.c_int),
                 ("split_num", ctypes.c_int), ("split_den", ctypes.c_int),
-                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+                ("trace", ctypes.c_void_p), ("trace_bytes", ctypes.c_size_t)]
 
 
 class TosError(RuntimeError):
@@ -164,7 +165,7 @@ _SCHEDULES = {"cosched": TOS_SCHEDULE_COSCHED, "sequential": TOS_SCHEDULE_SEQUEN
 
 
 def make_opts(x_tile=32, split="valu", fallback="off", tau=0.0, descale=None,
-              fallback_tiles=None, schedule="cosched", share=None):
+              fallback_tiles=None, schedule="cosched", share=None, trace=None):
     """Options for tos_attn_fwd.  split names a tos_softmax_split value;
     share = (num, den) is the matrix unit's share of it (None: the default)."""
     op = tos_fwd_opts_default()
@@ -178,6 +179,8 @@ def make_opts(x_tile=32, split="valu", fallback="off", tau=0.0, descale=None,
         op.q_descale, op.k_descale, op.v_descale = (float(descale[n]) for n in ("q", "k", "v"))
     op.fallback_tiles = _ptr(fallback_tiles)
     op.schedule = _SCHEDULES[schedule]
+    if trace is not None:   # a zeroed uint64 device buffer for the phase stamps
+        op.trace, op.trace_bytes = _ptr(trace), trace.numel() * trace.element_size()
     return op
 
 
@@ -252,7 +255,7 @@ def check_tensors(q, k, v, dtype=None, out=None, lse=None, fallback_tiles=None):
 def attn_fwd(q, k, v, causal=False, scale=None, dtype=None, x_tile=32, split="valu",
              fallback="off", tau=0.0, descale=None, with_lse=True, fallback_tiles=None,
              out=None, lse=None, stream=None, schedule="cosched", share=None,
-             use_workspace=True):
+             use_workspace=True, trace=None):
     """Allocate O (and lse) with torch and run tos_attn_fwd on the current stream.
 
     With use_workspace (the default) a problem with fewer query blocks than
@@ -275,7 +278,7 @@ def attn_fwd(q, k, v, causal=False, scale=None, dtype=None, x_tile=32, split="va
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     if not with_lse:
         lse = None
-    op = make_opts(x_tile, split, fallback, tau, descale, fallback_tiles, schedule, share)
+    op = make_opts(x_tile, split, fallback, tau, descale, fallback_tiles, schedule, share, trace)
     if use_workspace:
         nbytes = tos_attn_fwd_workspace_size(B, H, N, d, causal, _DTYPE_CODES[dtype], op)
         if nbytes > 0:

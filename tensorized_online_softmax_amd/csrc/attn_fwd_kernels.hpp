@@ -94,6 +94,23 @@ struct FwdArgs {
   int split_c;
   int nunits;
   float* ws;
+  unsigned long long* trace;   // traced instances: per-wave phase cycles (kTraceSlots each)
+};
+
+// Phase accounting of the traced instances (TRACE = true): per wave, in
+// s_memtime cycles, slots of trace[(workgroup * 8 + wave) * kTraceSlots + i]:
+constexpr int kTraceSlots = 16;
+enum TraceSlot {
+  kTrWave = 0,       // from the wave's first stamp to its last
+  kTrSteadyN = 1,    // steady steps
+  kTrSteady = 2,     // their cycles, barrier to barrier
+  kTrPhaseA = 3,     //   phase A (S_{j+1} = K Q^T with the first units)
+  kTrPhaseB = 4,     //   phase B (P~V with the remaining units), up to the barrier
+  kTrSteadyWait = 5, //   the barrier
+  kTrEdgeN = 6,      // edge steps (first, last and idle steps of a wave)
+  kTrEdge = 7,       // their cycles
+  kTrEdgeSoftmax = 8,  //   the softmax section, before the step's matrix instructions
+  kTrEdgeWait = 9    //   the barrier
 };
 
 constexpr int kWaves = 4;
@@ -325,7 +342,10 @@ constexpr int kPlanScaleMfma = split_plan(0, 0, 16, false);
 // (softmax, then QK^T, then P~V), with no interleaving inside a wave.
 // PLAN: the split plan (split_plan above).  A plan that puts O rescale slices
 // on the matrix unit needs one alpha per wave (X = 32, no per-row fallback).
-template <typename E, int D, bool CAUSAL, int X, int PLAN, bool FB_AUTO, bool SEQ>
+// TRACE: phase stamps (s_memtime, each followed by a wait for it, at points where
+// no LDS read is pending or about to be waited for) accumulated per wave into
+// a.trace, for the vector-interval accounting; an instrumented copy, slower.
+template <typename E, int D, bool CAUSAL, int X, int PLAN, bool FB_AUTO, bool SEQ, bool TRACE = false>
 __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_h16(FwdArgs a) {
   constexpr int RS = plan_rs(PLAN);                   // row-sum steps on the matrix unit
   constexpr bool ROWSUM_ANY = RS > 0, ROWSUM_ALL = RS == 4;
@@ -534,6 +554,21 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_h16(FwdArgs a) {
     const char* vt = vring + slot * BLK;
 #pragma unroll
     for (int i = 0; i < NPV; ++i) pv_mfma(i, vread(vt, i), pk);
+  };
+
+  // ---- phase stamps (TRACE)
+  unsigned long long tr[10] = {};
+  unsigned long long t_first = 0, t_last = 0;
+  auto stamp = [&]() -> unsigned long long {
+    if constexpr (TRACE) {
+      unsigned long long t;
+      asm volatile("s_memtime %0\n\ts_waitcnt lgkmcnt(0)" : "=s"(t)::"memory");
+      if (t_first == 0) t_first = t;
+      t_last = t;
+      return t;
+    } else {
+      return 0;
+    }
   };
 
   // ---- the softmax of one key block, in pieces (Algorithm 1)
@@ -771,6 +806,7 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_h16(FwdArgs a) {
   // last step (j = jend) loads nothing when the next item is prefetched: its
   // K slot holds the next item's first block.
   auto edge_step = [&](int j) {
+    const unsigned long long e0 = stamp();
     if (pref_next && j == jend)
       load_q(head_n, qrow_n, qvalid_n);
     else
@@ -788,9 +824,18 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_h16(FwdArgs a) {
       for (int k = 0; k < 16; ++k) exp_unit(k, S[0][0], S[0][1], P[0], nb);
       sums_commit(alpha, false);
     }
+    const unsigned long long e1 = stamp();
     if (j + 1 < jend_w) qk((j + 1) % kRing, S[0][0], S[0][1]);
     if (j >= 1 && j <= jend_w) pv((j - 1) % kRing, P[1]);
+    const unsigned long long e2 = stamp();
     step_barrier<2 * NV_STEP>();
+    if constexpr (TRACE) {
+      const unsigned long long e3 = stamp();
+      tr[kTrEdgeN] += 1;
+      tr[kTrEdge] += e3 - e0;
+      tr[kTrEdgeSoftmax] += e1 - e0;
+      tr[kTrEdgeWait] += e3 - e2;
+    }
     if (j < jend_w) rescale(alpha);
 #pragma unroll
     for (int t = 0; t < 4; ++t) P[1][t] = P[0][t];
@@ -853,6 +898,7 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_h16(FwdArgs a) {
     const char* kt = smem + ((u + 2) % kRing) * BLK;    // K_{j+1}
     const char* vt = vring + (u % kRing) * BLK;         // V_{j-1}
     f32x16 &c0 = S[cur][0], &c1 = S[cur][1], &n0 = S[nxt][0], &n1 = S[nxt][1];
+    const unsigned long long s0 = stamp();
     step_loads(j, XING);
     ev8 kop[LA], vop[LA];
 #pragma unroll
@@ -875,6 +921,7 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_h16(FwdArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_s_setprio(0);
+    const unsigned long long s1 = stamp();
     // phase B: units EA..15 start spread over the chunks
 #pragma unroll
     for (int i = 0; i < NPV; ++i) {
@@ -891,7 +938,16 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_h16(FwdArgs a) {
     pin(P[cur][3]);
     pin(lexact);
     if constexpr (!ROWSUM_ALL) pin(lsum);
+    const unsigned long long s2 = stamp();
     step_barrier<2 * NV_STEP>();
+    if constexpr (TRACE) {
+      const unsigned long long s3 = stamp();
+      tr[kTrSteadyN] += 1;
+      tr[kTrSteady] += s3 - s0;
+      tr[kTrPhaseA] += s1 - s0;
+      tr[kTrPhaseB] += s2 - s1;
+      tr[kTrSteadyWait] += s3 - s2;
+    }
     rescale(alpha);
   };
 
@@ -1051,6 +1107,15 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_h16(FwdArgs a) {
     finish();
     if (it_next >= nunits) {
       flush();
+      if constexpr (TRACE) {
+        stamp();
+        tr[kTrWave] = t_last - t_first;
+        if (lane == 0) {
+          unsigned long long* out = a.trace + ((size_t)gid * kPWaves + w) * kTraceSlots;
+#pragma unroll
+          for (int i = 0; i < 10; ++i) out[i] = tr[i];
+        }
+      }
       break;
     }
     pref = pref_next;

@@ -16,6 +16,7 @@ struct KernelChoice {
                      // kernels; fp8 always sums on the matrix unit, fp32 never
   bool fb_auto;      // fallback AUTO (x > 1 only)
   bool seq = false;  // sequential schedule (16-bit kernels, x = 1 or 32, vector row sum, no AUTO)
+  bool trace = false;   // the phase-stamped instances (bf16, d = 128, the ablation's settings)
 };
 
 // Workgroups of a persistent launch over `nitems` items: one per compute unit

@@ -14,6 +14,7 @@ template <typename E, int D>
 struct H16 {
   static hipError_t main(const FwdArgs& a, const KernelChoice& k, hipStream_t s);
   static hipError_t ablation(const FwdArgs& a, const KernelChoice& k, hipStream_t s);
+  static hipError_t traced(const FwdArgs& a, const KernelChoice& k, hipStream_t s);
 };
 
 // Is this choice one of the ablation instances?
@@ -22,7 +23,7 @@ inline bool h16_is_ablation(const KernelChoice& k) {
 }
 
 #ifdef TOS_H16_DEFINE
-template <typename E, int D, bool CAUSAL, int X, int PLAN, bool FB, bool SEQ = false>
+template <typename E, int D, bool CAUSAL, int X, int PLAN, bool FB, bool SEQ = false, bool TRACE = false>
 static hipError_t go_h16(const FwdArgs& a, hipStream_t s) {
   FwdArgs arg = a;
   arg.nqb = (a.N + kPBr - 1) / kPBr;
@@ -31,7 +32,7 @@ static hipError_t go_h16(const FwdArgs& a, hipStream_t s) {
   // hipLaunchKernel reports this launch's own status (hipGetLastError could
   // return an error left behind by an earlier, unrelated call)
   void* params[] = {&arg};
-  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&attn_fwd_h16<E, D, CAUSAL, X, PLAN, FB, SEQ>),
+  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&attn_fwd_h16<E, D, CAUSAL, X, PLAN, FB, SEQ, TRACE>),
                                  grid, block, params, 0, s);
   if (e != hipSuccess || arg.split_c <= 0) return e;
   // the pieces' partial results, merged per item on the same stream
@@ -99,6 +100,32 @@ static hipError_t abl_by_x(const FwdArgs& a, const KernelChoice& k, hipStream_t 
   }
   if (k.x != 32 || k.fb_auto) return hipErrorNotSupported;
   return abl_plan<E, D, CAUSAL>(a, k, s);
+}
+
+// the phase-stamped instances: the settings of the vector-interval table
+// (per-row and tile-32 sequential, per-row, tile-16 and tile-32 co-scheduled,
+// matrix-unit row sum, everything on the matrix unit), fallback off
+template <typename E, int D, bool CAUSAL>
+static hipError_t traced_by_x(const FwdArgs& a, const KernelChoice& k, hipStream_t s) {
+  constexpr int V = kPlanValu, R = kPlanRowsumMfma, A = split_plan(4, 16, 16, false);
+  if (k.fb_auto) return hipErrorNotSupported;
+  if (k.seq) {
+    if (k.plan != V) return hipErrorNotSupported;
+    if (k.x == 1) return go_h16<E, D, CAUSAL, 1, V, false, true, true>(a, s);
+    if (k.x == 32) return go_h16<E, D, CAUSAL, 32, V, false, true, true>(a, s);
+    return hipErrorNotSupported;
+  }
+  if (k.x == 1 && k.plan == V) return go_h16<E, D, CAUSAL, 1, V, false, false, true>(a, s);
+  if (k.x == 16 && k.plan == V) return go_h16<E, D, CAUSAL, 16, V, false, false, true>(a, s);
+  if (k.x == 32 && k.plan == V) return go_h16<E, D, CAUSAL, 32, V, false, false, true>(a, s);
+  if (k.x == 32 && k.plan == R) return go_h16<E, D, CAUSAL, 32, R, false, false, true>(a, s);
+  if (k.x == 32 && k.plan == A) return go_h16<E, D, CAUSAL, 32, A, false, false, true>(a, s);
+  return hipErrorNotSupported;
+}
+
+template <typename E, int D>
+hipError_t H16<E, D>::traced(const FwdArgs& a, const KernelChoice& k, hipStream_t s) {
+  return k.causal ? traced_by_x<E, D, true>(a, k, s) : traced_by_x<E, D, false>(a, k, s);
 }
 
 template <typename E, int D>

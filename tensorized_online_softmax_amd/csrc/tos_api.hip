@@ -170,6 +170,15 @@ tos_status prepare(const tos_fwd_opts* opts, int64_t B, int64_t H, int64_t N, in
   }
   // fp8 sums on the matrix unit whatever the option
   if (dtype == TOS_FP8_E4M3) kc.plan = tos::kPlanValu;
+  // the phase-stamped instances
+  if (op.trace != nullptr) {
+    if (dtype != TOS_BF16 || d != 128 || op.fallback != TOS_FALLBACK_OFF) return TOS_ERR_UNSUPPORTED;
+    if (op.trace_bytes < (size_t)tos::device_cus() * tos::kPWaves * tos::kTraceSlots * sizeof(uint64_t))
+      return TOS_ERR_INVALID_ARG;
+    kc.trace = true;
+  } else if (op.trace_bytes != 0) {
+    return TOS_ERR_INVALID_ARG;
+  }
   if (kc.seq && (!h16 || kc.plan != tos::kPlanValu || kc.fb_auto || kc.x == 16 || kc.x == 64))
     return TOS_ERR_UNSUPPORTED;
   // X = 64 (tiles of two waves): the 16-bit kernels with the vector row sum
@@ -239,6 +248,10 @@ tos_status tos_attn_fwd(const void* q, const void* k, const void* v, void* o, fl
   if (overlaps(o, out_b, lse, lse_b)) return TOS_ERR_INVALID_ARG;
   if (overlaps(op.workspace, ws_b, o, out_b) || overlaps(op.workspace, ws_b, lse, lse_b))
     return TOS_ERR_INVALID_ARG;
+  for (const void* t : {q, k, v, (const void*)o, (const void*)lse, (const void*)op.workspace}) {
+    const size_t tb = t == o ? out_b : t == lse ? lse_b : t == op.workspace ? ws_b : in_b;
+    if (overlaps(op.trace, op.trace_bytes, t, tb)) return TOS_ERR_INVALID_ARG;
+  }
 
   tos::FwdArgs a;
   a.q = q;
@@ -275,6 +288,7 @@ tos_status tos_attn_fwd(const void* q, const void* k, const void* v, void* o, fl
     a.ws = (float*)op.workspace;
   }
   a.nunits = (int)(BH * nqb);
+  a.trace = (unsigned long long*)op.trace;
 
   const hipStream_t s = (hipStream_t)stream;
   hipError_t e = hipErrorNotSupported;

@@ -149,6 +149,45 @@ def test_key_pieces(dtype, B, H, N, d, causal, x_tile, with_lse):
                  f"whole blocks {dtype} B={B} H={H} N={N} d={d}")
 
 
+# The phase-stamped instances (vector-interval accounting) compute the same
+# attention, and account every step of every wave: with one item per
+# workgroup, a wave runs one step per key block of the item plus one.
+TRACED = [(1, "valu", "sequential"), (32, "valu", "sequential"), (1, "valu", "cosched"),
+          (16, "valu", "cosched"), (32, "valu", "cosched"), (32, "rowsum_mfma", "cosched"),
+          (32, "all_mfma", "cosched")]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("x_tile,split,schedule", TRACED)
+def test_traced_instances(x_tile, split, schedule, causal):
+    B, H, N, d = 1, 3, 1000, 128
+    inp = _inp(B, H, N, d, "bf16", seed=610 + x_tile)
+    dev = to_device(inp)
+    trace = torch.zeros(1024 * 1024 // 8, dtype=torch.int64, device="cuda")
+    o, lse = tb.attn_fwd(dev["q"], dev["k"], dev["v"], causal=causal, scale=inp["scale"],
+                         x_tile=x_tile, split=split, schedule=schedule, trace=trace,
+                         use_workspace=False)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle_exact(inp, causal)
+    assert_close(o.to(torch.float64).cpu().numpy().reshape(o_ref.shape), o_ref,
+                 lse.to(torch.float64).cpu().numpy().reshape(lse_ref.shape), lse_ref, "bf16",
+                 f"traced X={x_tile} {split} {schedule} causal={causal}")
+    tr = trace.view(-1, 16).cpu().numpy()
+    nqb = (N + 255) // 256
+    items = B * H * nqb                       # one item per workgroup here
+    used = tr[: items * 8]
+    assert np.all(used[:, 0] > 0) and np.all(tr[items * 8:] == 0)
+    for it in range(items):
+        qb = (nqb - 1 - it // (B * H)) if causal else it // (B * H)
+        nblk = (min((qb + 1) * 256, N) - 1) // 64 + 1 if causal else (N + 63) // 64
+        steps = used[it * 8: (it + 1) * 8, 1] + used[it * 8: (it + 1) * 8, 6]
+        assert np.all(steps == nblk + 1), (it, steps, nblk)
+        # phases within their steps
+        w = used[it * 8: (it + 1) * 8]
+        assert np.all(w[:, 3] + w[:, 4] + w[:, 5] <= w[:, 2] + 8 * w[:, 1])
+        assert np.all(w[:, 8] + w[:, 9] <= w[:, 7] + 8 * w[:, 6])
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32", "fp8"])
 def test_without_lse(dtype):
     """lse = NULL: O is the same as with lse, and matches the oracle."""
