@@ -735,17 +735,27 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_h16(FwdArgs a) {
   // surrogate, and there an unrounded sum next to a flushed numerator would
   // shrink O towards 0 instead of leaving the surviving terms' average.
   constexpr bool STEADY_EXACT = PLAN == kPlanValu && Elem16<E>::kPreLog2 == 0;
+  // With the whole row sum on the matrix unit (ones x P~^T for every block,
+  // the normaliser of O), a steady step takes no vector sum at all: lse then
+  // uses the rounded sum of the steady blocks, plus, from the edge steps, the
+  // unrounded sums of their blocks (kept as a correction: unrounded minus
+  // rounded).  A row with steady blocks has more than 128 keys, and its lse
+  // is then at least ln 128, where the rounding of P~ (2^-9 relative at most)
+  // stays inside the relative bound of lse.
+  constexpr bool LEAN = PLAN == kPlanRowsumMfma;
   auto unit_sum_pack = [&](int k, ev8* pk, bool steady) {
     const int t = k / 8, r = 2 * (k % 8);
     const float p0 = up[k][0], p1 = up[k][1];
-    pe[t] += p0;
-    pe[t] += p1;
+    if (!(LEAN && steady)) {
+      pe[t] += p0;
+      pe[t] += p1;
+    }
     ev2 w;
     w[0] = (E)p0;
     w[1] = (E)p1;
     pk[2 * t + r / 8][r % 8] = w[0];
     pk[2 * t + r / 8][r % 8 + 1] = w[1];
-    if (!(steady && STEADY_EXACT) && !rs_on_mfma(PLAN, 2 * t + r / 8))
+    if ((LEAN && !steady) || (!(steady && STEADY_EXACT) && !rs_on_mfma(PLAN, 2 * t + r / 8)))
       ps[t] = Elem16<E>::dot2(w, ones2, ps[t]);
   };
   auto exp_unit = [&](int k, const f32x16& s0, const f32x16& s1, ev8* pk, float nb) {
@@ -756,6 +766,10 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_h16(FwdArgs a) {
   // the block's sums into the running ones (which absorb alpha here; O and the
   // MFMA row sum get alpha at the end of the step)
   auto sums_commit = [&](float alpha, bool steady) {
+    if constexpr (LEAN) {   // lexact holds the edge blocks' unrounded-minus-rounded sums
+      lexact = steady ? lexact * alpha : lexact * alpha + ((pe[0] + pe[1]) - (ps[0] + ps[1]));
+      return;
+    }
     const float e = pe[0] + pe[1];
     lexact = lexact * alpha + e;
     if constexpr (!ROWSUM_ALL) lsum = lsum * alpha + ((steady && STEADY_EXACT) ? e : ps[0] + ps[1]);
@@ -969,7 +983,8 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_h16(FwdArgs a) {
     float l = 0.0f;
     if constexpr (ROWSUM_ANY) l = lacc[0];
     if constexpr (!ROWSUM_ALL) l += pair_reduce(lsum, [](float x, float y) { return x + y; });
-    const float le = pair_reduce(lexact, [](float x, float y) { return x + y; });
+    float le = pair_reduce(lexact, [](float x, float y) { return x + y; });
+    if constexpr (LEAN) le += l;
     const float inv = l > 0.0f ? a.o_scale / l : 0.0f;
     const float lse_v = le > 0.0f ? a.lse_scale * st.ref + (__logf(le) - (float)Elem16<E>::kPreLog2 * 0.69314718f)
                                   : -__builtin_inff();
