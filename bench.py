@@ -355,8 +355,8 @@ VECTOR_INTERVAL = [
 
 
 def vector_interval(workload, steps, warmup):
-    """Phase-stamped runs of each setting (s_memtime cycles per wave, summed over
-    the launches): the step cycles of a SIMD against its matrix-unit cycles give
+    """Phase-stamped runs of each setting (s_memtime cycles per wave, as the last
+    launch wrote them): the step cycles of a SIMD against its matrix-unit cycles give
     the share of the step in which the matrix unit is idle; the sequential
     schedule's softmax section is its vector-only time.  The stamps wait for
     themselves, so a traced launch is slower than a plain one (both reported)."""
@@ -390,8 +390,9 @@ def vector_interval(workload, steps, warmup):
             torch.cuda.synchronize()
             t = sorted(ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(n))
             times[kind] = t[len(t) // 2]
-        tr = trace.view(-1, 16).cpu().numpy().astype("float64")
-        tr = tr[tr[:, 0] > 0]
+        raw = trace.view(-1, 16).cpu().numpy()
+        raw = raw[raw[:, 0] > 0]
+        tr = raw.astype("float64")
         tot = tr.sum(axis=0)
         line = {"workload": w.name, "setting": name, "x_tile": x, "softmax_split": split,
                 "schedule": sched, "launches": n,
@@ -408,6 +409,16 @@ def vector_interval(workload, steps, warmup):
             line.update({"edge_steps": int(tot[6]), "edge_step_clk": round(tot[7] / tot[6], 1),
                          "edge_softmax_clk": round(tot[8] / tot[6], 1),
                          "edge_barrier_clk": round(tot[9] / tot[6], 1)})
+        # the shader clock from the wave spans against the fixed 100 MHz counter;
+        # the last launch's span (its waves' first to last stamps on that counter)
+        # against each wave's own: the share of the launch a wave is running
+        line["shader_clock_ghz"] = round(tot[0] / tot[10] * 0.1, 3)
+        line["wave_clk"] = round(tot[0] / tr.shape[0], 1)
+        line["steps_share_of_wave"] = round((tot[2] + tot[7]) / tot[0], 4)
+        span = int(raw[:, 12].max()) - int(raw[:, 11].min())
+        if span > 0:
+            line["launch_span_us"] = round(span / 100.0, 2)
+            line["wave_span_share_mean"] = round(float(tot[10] / tr.shape[0]) / span, 4)
         # the matrix unit's idle share of a step of a SIMD (two waves), from the
         # steady steps when the schedule has them, else from all steps
         step = line.get("steady_step_clk") or line.get("edge_step_clk")

@@ -174,12 +174,15 @@ typedef struct {
                               fallback off; X = 1 / 16 / 32 co-scheduled, X = 1 /
                               32 sequential, or X = 32 with the matrix-unit row
                               sum or everything on the matrix unit; else
-                              TOS_ERR_UNSUPPORTED) that adds, per wave, s_memtime
+                              TOS_ERR_UNSUPPORTED) that writes, per wave, s_memtime
                               cycles of its steps and their phases to 16 slots at
                               trace[(workgroup * 8 + wave) * 16]: 0 wave total,
                               1 steady steps, 2 their cycles, 3 phase A, 4 phase
                               B, 5 barrier wait, 6 edge steps, 7 their cycles,
-                              8 their softmax section, 9 barrier wait.  The
+                              8 their softmax section, 9 barrier wait, 10 the
+                              wave total in s_memrealtime ticks (100 MHz), 11 /
+                              12 s_memrealtime at the wave's first and last
+                              stamp (13-15 unused).  The
                               buffer holds one workgroup per compute unit:
                               trace_bytes >= compute units * 1024 (else
                               TOS_ERR_INVALID_ARG); the caller zeroes it     */

@@ -285,7 +285,18 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_fp8(FwdArgs a) {
     bm = qvalid ? bm : -__builtin_inff();
     row_max_update(st, bm);
   };
-  auto tile_ref = [&]() { ref_new = block_ref<X, FB_AUTO>(st, c, tau); };
+  auto tile_ref = [&]() {
+    if constexpr (FB_AUTO && X > 1) {
+      // a tile that went per-row stays so: once every tile of the wave has
+      // (most tiles of data with spiky rows), the tile maximum and minimum
+      // are not needed any more (a uniform branch)
+      if (__builtin_amdgcn_ballot_w64(!st.per_row) == 0) {
+        ref_new = st.m_run;
+        return;
+      }
+    }
+    ref_new = block_ref<X, FB_AUTO>(st, c, tau);
+  };
   // alpha, and -c*ref + 8: the 2^8 pre-scale rides on the exponent
   auto advance = [&](float& alpha, float& nb) {
     alpha = ref_advance(st, ref_new, c);

@@ -110,7 +110,10 @@ enum TraceSlot {
   kTrEdgeN = 6,      // edge steps (first, last and idle steps of a wave)
   kTrEdge = 7,       // their cycles
   kTrEdgeSoftmax = 8,  //   the softmax section, before the step's matrix instructions
-  kTrEdgeWait = 9    //   the barrier
+  kTrEdgeWait = 9,   //   the barrier
+  kTrRealtime = 10,  // kTrWave's span in s_memrealtime ticks (a fixed 100 MHz clock)
+  kTrRtFirst = 11,   // s_memrealtime at the wave's first and last stamps (one clock
+  kTrRtLast = 12     // for the whole chip: the launch's span and each wave's place in it)
 };
 
 constexpr int kWaves = 4;
@@ -557,13 +560,18 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_h16(FwdArgs a) {
   };
 
   // ---- phase stamps (TRACE)
-  unsigned long long tr[10] = {};
-  unsigned long long t_first = 0, t_last = 0;
+  unsigned long long tr[kTraceSlots] = {};
+  unsigned long long t_first = 0, t_last = 0, rt_first = 0;
+  auto realtime = [&]() -> unsigned long long {
+    unsigned long long t;
+    asm volatile("s_memrealtime %0\n\ts_waitcnt lgkmcnt(0)" : "=s"(t)::"memory");
+    return t;
+  };
+  // (branch-free: the wave's first stamps are taken once, before its first unit)
   auto stamp = [&]() -> unsigned long long {
     if constexpr (TRACE) {
       unsigned long long t;
       asm volatile("s_memtime %0\n\ts_waitcnt lgkmcnt(0)" : "=s"(t)::"memory");
-      if (t_first == 0) t_first = t;
       t_last = t;
       return t;
     } else {
@@ -1051,6 +1059,10 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_h16(FwdArgs a) {
   if constexpr (X == 64) {   // sequence numbers start at 1: clear them (the
     if (lane == 0) ((int*)xslot)[4 * w + 2] = 0;   // first barrier publishes it)
   }
+  if constexpr (TRACE) {
+    t_first = stamp();
+    rt_first = realtime();
+  }
   int it = item_of(0, gid, nwg);
   set_item(it);
   bool pref = false;   // this item's first blocks are in the rings already
@@ -1125,10 +1137,13 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_h16(FwdArgs a) {
       if constexpr (TRACE) {
         stamp();
         tr[kTrWave] = t_last - t_first;
+        tr[kTrRtFirst] = rt_first;
+        tr[kTrRtLast] = realtime();
+        tr[kTrRealtime] = tr[kTrRtLast] - rt_first;
         if (lane == 0) {
           unsigned long long* out = a.trace + ((size_t)gid * kPWaves + w) * kTraceSlots;
 #pragma unroll
-          for (int i = 0; i < 10; ++i) out[i] = tr[i];
+          for (int i = 0; i < kTraceSlots; ++i) out[i] = tr[i];
         }
       }
       break;

@@ -186,6 +186,12 @@ def test_traced_instances(x_tile, split, schedule, causal):
         w = used[it * 8: (it + 1) * 8]
         assert np.all(w[:, 3] + w[:, 4] + w[:, 5] <= w[:, 2] + 8 * w[:, 1])
         assert np.all(w[:, 8] + w[:, 9] <= w[:, 7] + 8 * w[:, 6])
+        # the steps within the wave's span, which the fixed 100 MHz clock
+        # measures too (a shader clock of 0.5-3.5 GHz)
+        assert np.all(w[:, 2] + w[:, 7] <= w[:, 0])
+        assert np.all(w[:, 12] - w[:, 11] == w[:, 10])
+        clk = w[:, 0] / w[:, 10] * 0.1
+        assert np.all((clk > 0.5) & (clk < 3.5)), clk
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32", "fp8"])
