@@ -208,8 +208,8 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_fp8(FwdArgs a) {
   RowState st;
   const float c = a.c, tau = a.tau;
   f32x16 oacc[NMT];
-  f32x16 lacc;      // row sum of hi + lo of 2^8 P~ over the edge steps (MFMA;
-                    // every register holds it)
+  float ledge;      // row sum of hi + lo of 2^8 P~ over the edge steps (from
+                    // the matrix unit; both lanes of the pair hold it)
   float lsteady;    // row sum of the unrounded 2^8 P~ over the steady steps
                     // (this lane's keys only)
   float lexact;     // row sum of the unrounded 2^8 P~ (this lane's keys only)
@@ -343,7 +343,7 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_fp8(FwdArgs a) {
     if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
 #pragma unroll
       for (int mt = 0; mt < NMT; ++mt) oacc[mt] *= alpha;
-      lacc *= alpha;
+      ledge *= alpha;
     }
   };
   auto step_loads = [&](int j, auto XING) {
@@ -382,8 +382,9 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_fp8(FwdArgs a) {
       rescale(alpha);
       // this block's rounded row sum (ones x (hi + lo)^T), after the rescale:
       // its terms are relative to the new reference already
-      lacc = mfma_f8(ones, PH[0], lacc);
-      lacc = mfma_f8(ones, PL[0], lacc);
+      // (every register of the product holds the sum: one float carries it,
+      // and the rescales multiply one float instead of sixteen)
+      ledge += mfma_f8(ones, PL[0], mfma_f8(ones, PH[0], f32x16{}))[0];
     }
     PH[1] = PH[0];
     PL[1] = PL[0];
@@ -492,7 +493,7 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_fp8(FwdArgs a) {
   int o_nrows = 0;
   float lse_out = 0.0f;
   auto finish = [&]() {
-    const float l = lacc[0] + pair_reduce(lsteady, [](float x, float y) { return x + y; });
+    const float l = ledge + pair_reduce(lsteady, [](float x, float y) { return x + y; });
     const float le = pair_reduce(lexact, [](float x, float y) { return x + y; });
     const float inv = l > 0.0f ? a.o_scale / l : 0.0f;
     int sr = ln;
@@ -548,7 +549,7 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_fp8(FwdArgs a) {
     row_state_init(st, X == 1);
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt) oacc[mt] = f32x16{};
-    lacc = f32x16{};
+    ledge = 0.0f;
     lsteady = 0.0f;
     lexact = 0.0f;
     S[0][0] = S[0][1] = S[1][0] = S[1][1] = f32x16{};
