@@ -34,7 +34,8 @@ _CSRC = "tensorized_online_softmax_amd/csrc/"
 KERNEL_SOURCES = {
     "bf16": [_CSRC + f for f in ("attn_fwd_kernels.hpp", "softmax_tile.hpp", "pieces.hpp")],
     "f16": [_CSRC + f for f in ("attn_fwd_kernels.hpp", "softmax_tile.hpp", "pieces.hpp")],
-    "f32": [_CSRC + f for f in ("attn_fwd_kernels.hpp", "softmax_tile.hpp", "pieces.hpp")],
+    "f32": [_CSRC + f for f in ("attn_fwd_kernels.hpp", "attn_fwd_f32_slab.hpp", "softmax_tile.hpp",
+                                "pieces.hpp")],
     "fp8": [_CSRC + f for f in ("attn_fwd_kernels.hpp", "attn_fwd_fp8.hpp", "softmax_tile.hpp",
                                 "pieces.hpp")],
 }
@@ -66,6 +67,23 @@ def read_traffic(workload, dtype):
         return float(vals["hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def block_shape(w, x_tile, fallback):
+    """Query rows and keys per step of the kernel the library picks for the
+    workload: fp32 at X = 1 or 16 without the fallback runs in 16-row slabs of
+    16-key chunks (with 1, 2 or 4 workgroups sharing the head dim) while 128-row
+    workgroups would number fewer than the compute units; other fp32 calls take
+    128-row workgroups, the 16-bit and fp8 kernels 256-row ones, of 64-key blocks."""
+    import torch
+    if w.dtype != "f32":
+        return {"Br": 256, "Bc": 64}
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    BH = w.B * w.H
+    if x_tile in (1, 16) and fallback == "off" and BH * -(-w.N // 128) < cus:
+        slabs = BH * -(-w.N // 16)
+        return {"Br": 16, "Bc": 16, "head_dim_shares": 4 if 4 * slabs <= cus else 2 if 2 * slabs <= cus else 1}
+    return {"Br": 128, "Bc": 64}
 
 
 def cpu_model():
@@ -330,7 +348,7 @@ def time_workload(w, inp, x_tile, split, fallback, schedule, share, steps, warmu
               "softmax_split": "rowsum_mfma" if w.dtype == "fp8" else split,
               "share": f"{share[0]}/{share[1]}" if share else None,
               "schedule": schedule,
-              "fallback": fallback, "Br": 128 if w.dtype == "f32" else 256, "Bc": 64,
+              "fallback": fallback, **block_shape(w, x_tile, fallback),
               "flops_per_step": flops, "pct_of_peak": round(100 * achieved / peak, 2)}
     del q, k, v, o, lse
     return {"value": round(flops / (ms_per_step / 1e3) / 1e12, 2),

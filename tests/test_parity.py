@@ -352,6 +352,33 @@ def test_fp8_spiky_needs_the_fallback():
     assert np.all(switched[bh, row // 32])
 
 
+# fp32 problems whose 128-row workgroups would number fewer than the compute
+# units run in 16-row slabs, each slab's keys split across the workgroup's 4
+# waves and merged by lse (X = 1 and 16), with the head dim shared among 4, 2
+# or 1 workgroups as the grid allows (on 256 compute units: 4 up to N = 1024 of
+# one head, 2 at N = 1500, 1 at N = 2100); more heads take the 128-row kernel
+# (the last case).  Ragged N gives waves without a chunk, with one chunk, and
+# with several (the next chunk's loads in flight).
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("x_tile", [1, 16])
+@pytest.mark.parametrize("B,H,N", [(1, 1, 1), (1, 1, 17), (1, 1, 128), (1, 2, 130), (2, 1, 383),
+                                   (1, 1, 1000), (1, 1, 1500), (1, 1, 2100), (1, 260, 130)])
+def test_f32_slabs(d, causal, x_tile, B, H, N):
+    inp = _inp(B, H, N, d, "f32", seed=500 + N + d + x_tile)
+    o_ref, lse_ref = oracle_exact(inp, causal)
+    o, lse, _ = run_gpu(inp, causal, x_tile=x_tile)
+    assert_close(o.reshape(o_ref.shape), o_ref, lse.reshape(lse_ref.shape), lse_ref, "f32",
+                 f"f32 slabs d={d} causal={causal} X={x_tile} B={B} H={H} N={N}")
+    if N == 383:   # without lse: O alone
+        dev = to_device(inp)
+        o2, none = tb.attn_fwd(dev["q"], dev["k"], dev["v"], causal=causal, scale=inp["scale"],
+                               x_tile=x_tile, with_lse=False)
+        torch.cuda.synchronize()
+        assert none is None
+        assert torch.equal(o2.cpu(), torch.from_numpy(o).to(torch.float32).reshape(o2.shape))
+
+
 @pytest.mark.parametrize("name", ["single_head_f32", "mha_bf16", "causal_bf16",
                                   "causal_bf16_shard8", "long_causal_bf16", "fp8_spiky",
                                   "causal_f16"])
