@@ -447,6 +447,61 @@ def vector_interval(workload, steps, warmup):
         print(json.dumps(line), flush=True)
 
 
+def item_cost(steps, warmup):
+    """Plain launches of the persistent bf16 kernel (d = 128, not causal, X = 32)
+    with k = 1, 2, 4 and 8 items per workgroup (256-row query blocks; k times
+    the compute-unit count of them) of s = N/64 key-block steps, N = 1024 and
+    4096, each timed over interleaved rounds; then the least-squares fit
+    time = a + k * (c_item + s * c_step): what a key-block step and an item's
+    boundary (its prologue, first and last steps, epilogue) cost on this GPU."""
+    import numpy as np
+    import torch
+    from tensorized_online_softmax_amd import binding
+    torch.cuda.set_device(0)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    stream = torch.cuda.current_stream()
+    cases = []
+    for N in (1024, 4096):
+        for k in (1, 2, 4, 8):
+            BH = k * cus * 256 // N
+            g = torch.Generator(device="cuda").manual_seed(BH * 7 + N)
+            q, kk, v = (torch.randn(1, BH, N, 128, device="cuda", generator=g).to(torch.bfloat16)
+                        for _ in range(3))
+            o = torch.empty_like(q)
+            lse = torch.empty(1, BH, N, device="cuda")
+            cases.append({"N": N, "items_per_workgroup": k, "steps_per_item": N // 64, "heads": BH,
+                          "t": [], "f": (lambda q=q, kk=kk, v=v, o=o, lse=lse: binding.attn_fwd(
+                              q, kk, v, causal=False, out=o, lse=lse))})
+    n = max(5, min(steps, 20))
+    for c in cases:
+        for _ in range(max(2, min(warmup, 5))):
+            c["f"]()
+    torch.cuda.synchronize()
+    for _ in range(3):   # rounds: the cases alternate, so that clock drift falls on all alike
+        for c in cases:
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+            for i in range(n):
+                ev[i].record(stream)
+                c["f"]()
+            ev[n].record(stream)
+            torch.cuda.synchronize()
+            c["t"] += [ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(n)]
+    for c in cases:
+        c["median_us"] = round(float(np.median(c["t"])), 2)
+    A = np.array([[1.0, c["items_per_workgroup"], c["items_per_workgroup"] * c["steps_per_item"]]
+                  for c in cases])
+    y = np.array([c["median_us"] for c in cases])
+    coef, *_ = np.linalg.lstsq(A, y, rcond=None)
+    out = {"metric": "per-item and per-step cost of the persistent bf16 kernel (d=128, not causal, X=32)",
+           "unit": "us", "compute_units": cus, "launches_per_case": 3 * n,
+           "cases": [{k: c[k] for k in ("N", "heads", "items_per_workgroup", "steps_per_item", "median_us")}
+                     for c in cases],
+           "fit": {"fixed_us": round(float(coef[0]), 2), "per_item_us": round(float(coef[1]), 2),
+                   "per_step_us": round(float(coef[2]), 3),
+                   "residuals_us": [round(float(r), 1) for r in y - A @ coef]}}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -479,6 +534,10 @@ def main():
                     help="instead of the attention bench: time torch's bf16 GEMM (the vendor "
                          "library) on random and on all-zero data, for the MFMA throughput this "
                          "GPU sustains under its power limit")
+    ap.add_argument("--item-cost", action="store_true",
+                    help="instead of the attention bench: plain launches of the bf16 d=128 kernel "
+                         "at 1, 2, 4 and 8 items per workgroup and two sequence lengths, fitted "
+                         "to a per-step and a per-item cost; one JSON line")
     ap.add_argument("--vector-interval", action="store_true",
                     help="instead of the attention bench: phase-stamped runs of the ablation's "
                          "settings (bf16, d=128 workloads) and the matrix unit's idle share of "
@@ -486,6 +545,9 @@ def main():
     args = ap.parse_args()
     if args.vector_interval:
         vector_interval(args.workload, args.steps, args.warmup)
+        return
+    if args.item_cost:
+        item_cost(args.steps, args.warmup)
         return
     if args.mfma_ceiling:
         mfma_ceiling()
