@@ -32,6 +32,11 @@
  *     the caller (tos_fwd_opts.workspace, sized by tos_attn_fwd_workspace_size);
  *     without one the call runs whole query blocks, with the same results up
  *     to rounding.
+ *   - fp32 inputs at X = 1 or 16 without the fallback run, when 128-row
+ *     workgroups would number fewer than the compute units, in workgroups of
+ *     16 query rows whose waves split the keys and merge their partial
+ *     results exactly (the same rescale by exp(m_old - m_new)) in LDS, with
+ *     up to 4 workgroups sharing the head dim of O; no workspace is needed.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
  *     the call returns without synchronising.  A device fault surfaces at the
  *     caller's next synchronisation.
