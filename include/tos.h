@@ -224,8 +224,9 @@ tos_status tos_attn_fwd(const void* q, const void* k, const void* v, void* o, fl
  * memory (code under HIP graph capture, tight serving loops, harnesses that
  * forbid hipMalloc).  Same arguments and results; opts->workspace must be NULL
  * (TOS_ERR_INVALID_ARG otherwise): the pieces' workspace is a static device
- * array of 33.8 MB (256 x 256 x 129 floats, what any call with d <= 128 can
- * need), which each GPU the library runs on holds until the process ends.  A
+ * array of 17.3 MB (256 units x 256 rows x (2 x 128 + 8) bytes, what any call
+ * with d <= 128 can need), which each GPU the library runs on holds until the
+ * process ends.  A
  * call that would need more returns TOS_ERR_SCRATCH.  The call allocates
  * nothing; its first call on a device looks the array's address up.  Every
  * call on one GPU shares that array: calls that overlap in time on one GPU
@@ -240,7 +241,9 @@ tos_status tos_attn_fwd_noalloc(const void* q, const void* k, const void* v, voi
  * options (NULL = defaults) would use to cut query blocks into pieces on the
  * current device: 0 when the problem has enough query blocks to fill the
  * device, or the options rule it out (fp32 or fp8 inputs, a fallback other
- * than off).  At most 256 x 256 x (d + 1) x 4 bytes (33.8 MB at d = 128).
+ * than off).  At most 256 x 256 x (2d + 8) bytes (17.3 MB at d = 128): per
+ * unit, its partial O as fp16 rows, each scaled by a power of 2, then per row
+ * its lse and that power's exponent as floats.
  * Returns TOS_ERR_INVALID_ARG for a NULL bytes pointer or sizes/options that
  * tos_attn_fwd would reject as invalid. */
 tos_status tos_attn_fwd_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d, int causal,

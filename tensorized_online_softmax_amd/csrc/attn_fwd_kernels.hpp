@@ -90,7 +90,7 @@ struct FwdArgs {
   int count_x;       // > 0: count the X-row tiles of this size as per-row (FORCE)
   // 16-bit kernels: items cut into pieces of at most split_c key blocks
   // (pieces.hpp; 0 = whole items), nunits work units in all, and the
-  // workspace of the pieces' partial results (piece_floats(d) per unit)
+  // workspace of the pieces' partial results (piece_bytes(d) per unit)
   int split_c;
   int nunits;
   float* ws;
@@ -997,20 +997,36 @@ __global__ __launch_bounds__(kPThreads, 1) void attn_fwd_h16(FwdArgs a) {
     const float lse_v = le > 0.0f ? a.lse_scale * st.ref + (__logf(le) - (float)Elem16<E>::kPreLog2 * 0.69314718f)
                                   : -__builtin_inff();
     if (part) {
-      // a piece of an item: its O (normalised by its own row sums, fp32) and
-      // lse go to the unit's workspace slot, for the merge kernel
-      float* slot = a.ws + (size_t)unit * piece_floats(D);
+      // a piece of an item: its O (normalised by its own row sums) and lse go
+      // to the unit's workspace slot, for the merge kernel.  O as fp16, the row
+      // scaled by 2^e so that its largest magnitude lies in [2^14, 2^15)
+      // (pieces.hpp); e follows lse.
+      char* slot = (char*)a.ws + (size_t)unit * piece_bytes(D);
       const int r = 32 * w + ln;
+      float mx = 0.0f;
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmax_raw(mx, __builtin_fabsf(oacc[mt][i]));
+      mx = pair_reduce(mx, MaxOp()) * inv;
+      // mx = f 2^k with f in [0.5, 1): e = 15 - k puts mx in [2^14, 2^15)
+      const int e = mx > 0.0f ? 15 - __builtin_amdgcn_frexp_expf(mx) : 0;
       if (qvalid) {
+        typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 #pragma unroll
         for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            const float4 ov = make_float4(oacc[mt][4 * g] * inv, oacc[mt][4 * g + 1] * inv,
-                                          oacc[mt][4 * g + 2] * inv, oacc[mt][4 * g + 3] * inv);
-            *(float4*)(slot + (size_t)r * D + 32 * mt + 8 * g + 4 * hf) = ov;
+            h4 hv;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) hv[u] = (_Float16)__builtin_ldexpf(oacc[mt][4 * g + u] * inv, e);
+            *(h4*)(slot + 2 * ((size_t)r * D + 32 * mt + 8 * g + 4 * hf)) = hv;
           }
-        if (hf == 0) slot[kPieceRows * D + r] = lse_v;
+        if (hf == 0) {
+          float* tail = (float*)(slot + piece_tail(D));
+          tail[r] = lse_v;
+          tail[kPieceRows + r] = (float)e;
+        }
       }
       o_nrows = 0;          // nothing for flush()
       lse_rows = nullptr;
@@ -1187,24 +1203,31 @@ __global__ __launch_bounds__(256) void attn_merge_h16(FwdArgs a) {
   const int r = (blockIdx.x % NWI) * RPW + t / TPR;
   const int row = qb * kPieceRows + r;
   if (row >= N) return;
-  const float* base = a.ws + (size_t)first * piece_floats(D);
-  const size_t stride = (size_t)piece_floats(D);
+  // the item's slots (pieces.hpp): fp16 rows scaled by 2^e, then lse and e
+  const char* base = (const char*)a.ws + (size_t)first * piece_bytes(D);
+  const size_t stride = (size_t)piece_bytes(D);
+  auto tail = [&](int c) { return (const float*)(base + c * stride + piece_tail(D)); };
+  // one pass over the pieces, online: the running maximum m of their lse and
+  // the sums taken against it, rescaled when it moves (no load waits for an
+  // earlier piece's, so all of them are in flight at once)
   float m = -__builtin_inff();
-  for (int c = 0; c < np; ++c) m = fmaxf(m, base[c * stride + kPieceRows * D + r]);
   float acc[8] = {};
   float sum = 0.0f;
-  if (m != -__builtin_inff()) {
+  typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 #pragma unroll 4
-    for (int c = 0; c < np; ++c) {
-      const float* slot = base + c * stride;
-      const float lc = slot[kPieceRows * D + r];
-      const float wgt = lc == -__builtin_inff() ? 0.0f : __expf(lc - m);
-      const float4 x0 = *(const float4*)(slot + (size_t)r * D + col);
-      const float4 x1 = *(const float4*)(slot + (size_t)r * D + col + 4);
-      sum += wgt;
-      acc[0] += wgt * x0.x; acc[1] += wgt * x0.y; acc[2] += wgt * x0.z; acc[3] += wgt * x0.w;
-      acc[4] += wgt * x1.x; acc[5] += wgt * x1.y; acc[6] += wgt * x1.z; acc[7] += wgt * x1.w;
-    }
+  for (int c = 0; c < np; ++c) {
+    const float lc = tail(c)[r], ec = tail(c)[kPieceRows + r];
+    const h8 x = *(const h8*)(base + c * stride + 2 * ((size_t)r * D + col));
+    if (lc == -__builtin_inff()) continue;
+    const float m_new = fmaxf(m, lc);
+    const float keep = __expf(m - m_new);   // 0 while m is -inf
+    const float wgt = __expf(lc - m_new);
+    sum = sum * keep + wgt;
+    // the row's scale 2^-e rides on its weight
+    const float ws = __builtin_ldexpf(wgt, -(int)ec);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc[u] = acc[u] * keep + ws * (float)x[u];
+    m = m_new;
   }
   const float inv = sum > 0.0f ? 1.0f / sum : 0.0f;
   typedef E ev8_t __attribute__((ext_vector_type(8)));

@@ -10,9 +10,9 @@
 
 namespace {
 
-// 256 units x 256 rows x (128 + 1) floats: the most the pieces of any call use
-// (at most kMaxPieces units, d <= 128)
-constexpr size_t kScratchBytes = (size_t)tos::kMaxPieces * tos::kPieceRows * (128 + 1) * sizeof(float);
+// 256 units x 256 rows x (2 x 128 + 8) bytes: the most the pieces of any call
+// use (at most kMaxPieces units, d <= 128)
+constexpr size_t kScratchBytes = (size_t)tos::kMaxPieces * (size_t)tos::piece_bytes(128);
 
 // Device storage of each GPU the library runs on (held until the process
 // ends).  In host code this name is only a stand-in: its device address comes

@@ -7,7 +7,7 @@
 //   lse = ln sum_c exp(lse_c),   O = sum_c exp(lse_c - lse) O_c,
 // the same rescale by exp(m_old - m) that the online softmax applies block by
 // block (FlashAttention-T, section A3, Fig 2(a)), here between key ranges.
-// Shared by the host (sizes) and the kernels (unit -> piece).
+// Shared by the host (sizes) and the kernels (unit -> piece, the slot layout).
 #pragma once
 #include <hip/hip_runtime.h>
 
@@ -76,7 +76,12 @@ __host__ __device__ inline long long units_of(int BH, int nqb, int N, bool causa
   return u;
 }
 
-// floats of workspace per unit: the partial O (256 rows x d) and its lse (256)
-__host__ __device__ inline long long piece_floats(int d) { return (long long)kPieceRows * (d + 1); }
+// Workspace per unit, in bytes: the partial O as fp16 (256 rows x d), each row
+// scaled by 2^e so that its largest magnitude lies in [2^14, 2^15) -- fp16's
+// 11 bits relative to the row's largest value, whatever the range of V --
+// then per row its lse (256 floats) and its e (256 floats).
+__host__ __device__ constexpr long long piece_bytes(int d) { return (long long)kPieceRows * (2 * d + 8); }
+// byte offset, within a unit's slot, of its 256 lse values (the e values follow)
+__host__ __device__ constexpr long long piece_tail(int d) { return (long long)kPieceRows * 2 * d; }
 
 }  // namespace tos

@@ -198,7 +198,7 @@ int split_for(const tos_fwd_opts& op, const tos::KernelChoice& kc, tos_dtype dty
   if (C <= 0) return 0;
   const int nqb = (int)((N + tos::kPieceRows - 1) / tos::kPieceRows);
   const long long units = tos::units_of((int)BH, nqb, (int)N, kc.causal, C);
-  *bytes = (size_t)units * (size_t)tos::piece_floats((int)d) * sizeof(float);
+  *bytes = (size_t)units * (size_t)tos::piece_bytes((int)d);
   return C;
 }
 

@@ -196,14 +196,14 @@ def test_binding_rejects_bad_tensors():
 
 def test_workspace_size():
     """Pieces only where query blocks are fewer than compute units (256 when no
-    device is visible), 16-bit inputs and the fallback off; at most
-    256 x 256 x (d + 1) floats."""
+    device is visible), 16-bit inputs and the fallback off; at most 256 units of
+    256 rows x (2d + 8) bytes (fp16 O, then lse and the row scale's exponent)."""
     ws = tb.tos_attn_fwd_workspace_size
-    cap = 256 * 256 * 129 * 4
+    cap = 256 * 256 * (2 * 128 + 8)
     assert ws(2, 4, 4096, 128, 1, tb.TOS_BF16) == cap      # one GPU's share of 8: 128 blocks
     assert ws(2, 32, 4096, 128, 1, tb.TOS_BF16) == 0       # 1024 query blocks
     assert ws(4, 16, 1024, 64, 0, tb.TOS_BF16) == 0        # 256 query blocks
-    assert 0 < ws(1, 4, 1000, 64, 1, tb.TOS_F16) <= 256 * 256 * 65 * 4
+    assert 0 < ws(1, 4, 1000, 64, 1, tb.TOS_F16) <= 256 * 256 * (2 * 64 + 8)
     assert ws(1, 1, 128, 64, 0, tb.TOS_BF16) == 0          # 2 key blocks: nothing to cut
     assert ws(1, 2, 4096, 128, 0, tb.TOS_F32) == 0
     assert ws(1, 2, 4096, 128, 0, tb.TOS_FP8_E4M3, opts(q_descale=1.0)) == 0
