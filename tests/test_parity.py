@@ -149,6 +149,30 @@ def test_key_pieces(dtype, B, H, N, d, causal, x_tile, with_lse):
                  f"whole blocks {dtype} B={B} H={H} N={N} d={d}")
 
 
+# V scaled by a power of 2 scales O by exactly that power, bit for bit, and
+# leaves lse alone: P~ and the row sums do not depend on V, every product and
+# sum of the P~V accumulation scales exactly, and so does the pieces' partial O
+# (fp16 rows scaled by their own power of 2: at 2^20 a plain fp16 partial would
+# overflow, at 2^-20 it would lose bits in fp16's subnormals).  Property of the
+# exact arithmetic, at the one-GPU share's size, pieces and whole blocks.
+@pytest.mark.parametrize("use_workspace", [True, False])
+@pytest.mark.parametrize("shift", [20, -20])
+def test_v_power_of_two_scaling(use_workspace, shift):
+    B, H, N, d = 2, 4, 4096, 128
+    assert tb.tos_attn_fwd_workspace_size(B, H, N, d, 1, tb.TOS_BF16, tb.make_opts()) > 0
+    inp = _inp(B, H, N, d, "bf16", seed=777)
+    dev = to_device(inp)
+    v2 = (dev["v"].float() * 2.0 ** shift).to(torch.bfloat16)
+    assert torch.equal(v2.float(), dev["v"].float() * 2.0 ** shift)   # exact in bf16
+    kw = dict(causal=True, scale=inp["scale"], use_workspace=use_workspace)
+    o1, lse1 = tb.attn_fwd(dev["q"], dev["k"], dev["v"], **kw)
+    o2, lse2 = tb.attn_fwd(dev["q"], dev["k"], v2, **kw)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o2.float()).all()
+    assert torch.equal(o2.float(), o1.float() * 2.0 ** shift)
+    assert torch.equal(lse2, lse1)
+
+
 # The phase-stamped instances (vector-interval accounting) compute the same
 # attention, and account every step of every wave: with one item per
 # workgroup, a wave runs one step per key block of the item plus one.
