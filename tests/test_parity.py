@@ -481,6 +481,29 @@ def test_persistent_rounds(dtype, B, H, N, d, causal):
                  f"{dtype} B={B} H={H} N={N} d={d} causal={causal}")
 
 
+# Without key pieces a head's O and lse do not depend on the other heads of
+# the call: bit for bit the same alone (one item per workgroup, every prologue
+# loading its own blocks) as among 64 heads that take two persistent rounds,
+# whose rings run on from one item into the next (the next item's first blocks
+# and Q prefetched where the block count allows it; N = 2000 also gives items
+# whose counts do not).
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "fp8"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_heads_independent(dtype, causal):
+    B, H, N, d = 2, 32, 2000, 128
+    inp = inputs.make(B, H, N, d, dtype, seed=1300 + causal)
+    dev = to_device(inp)
+    kw = dict(causal=causal, scale=inp["scale"], dtype=dtype, use_workspace=False,
+              descale=inp["descale"] if dtype == "fp8" else None)
+    o, lse = tb.attn_fwd(dev["q"], dev["k"], dev["v"], **kw)
+    for b, h in ((0, 0), (0, 1), (0, 17), (1, 8), (1, 31)):
+        one = {n: dev[n][b:b + 1, h:h + 1].contiguous() for n in ("q", "k", "v")}
+        o1, lse1 = tb.attn_fwd(one["q"], one["k"], one["v"], **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(o1[0, 0].float(), o[b, h].float()), (dtype, causal, b, h)
+        assert torch.equal(lse1[0, 0], lse[b, h]), (dtype, causal, b, h)
+
+
 @pytest.mark.parametrize("dtype,B,H,N,d", [
     ("bf16", 1, 300, 300, 128),
     ("bf16", 2, 160, 520, 64),
