@@ -6,12 +6,18 @@ softmax, both products, the epilogue) with inputs already resident in HBM.
 Default workload: causal bf16 attention, B=2, H=32, N=4096, d=128 (X = 32).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--split valu|rowsum_mfma] [--x-tile X] [--no-cpu-baseline]
-                    [--copy-calib-mib M]
+                    [--split PLAN] [--share NUM/DEN] [--schedule cosched|sequential]
+                    [--x-tile X] [--fallback off|auto|force] [--no-cpu-baseline]
+                    [--no-fp8] [--cpu-rows R] [--copy-calib-mib M]
 
 --copy-calib-mib M also runs one plain device-to-device copy of M MiB after the
 timed region; rocprofv3 counter runs of this command use it to calibrate the
 FETCH_SIZE / WRITE_SIZE counters against a kernel of known traffic.
+
+Other modes, each printing its own JSON lines instead of the bench line:
+--ablation (the knob settings, launch by launch), --grid DTYPES (the page's
+workload grid), --vector-interval (phase-stamped instances), --mfma-ceiling (the
+vendor bf16 GEMM), --item-cost (per-step and per-item cost from plain launches).
 """
 import argparse
 import hashlib
